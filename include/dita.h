@@ -1,0 +1,250 @@
+/*
+ * dita.h -- C ABI of the selective attention-state reuse library for MI355X (gfx950).
+ *
+ * One rank owns a query partition Q and attends to P key/value context
+ * partitions (K_p, V_p).  For every partition the rank either computes a
+ * fresh attention state (O_p, LSE_p) or reuses the state cached at an
+ * earlier denoising step; all P states are then merged exactly by their
+ * log-sum-exp weights.  Method: the web page "DiTango: Cost-Effective
+ * Parallel Diffusion Generation with Selective Attention State Reuse"
+ * (gist.science, paper 2607.15650), section Methodology:
+ *   - "2. State-Centric Parallel Runtime" > "State Composition": a state is an
+ *     output plus its log-sum-exp; states compose associatively and
+ *     commutatively; composed states are cached instead of raw K/V.
+ *   - "1. Anchor-Guided Selection Planner": each partition is computed fresh
+ *     or its historical state is reused; anchor steps recompute everything;
+ *     the local partition is always computed.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every function returns an int status (dita_status).  Nothing throws.
+ *  - Every argument is validated before any HIP call or kernel launch; on an
+ *    error nothing is launched and no output, slot or metadata changes.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and is asynchronous: no call synchronises the host.  Faults of
+ *    the kernels surface at the caller's next synchronisation.
+ *  - The caller owns every device buffer, the state-cache buffer included.
+ *    The library owns only the host-side cache handle.
+ *  - Layouts are contiguous row-major: Q and O are [B, H, Nq, D]; K_p and
+ *    V_p are [B, H, Nk_p, D]; LSE arrays are float32 [B, H, Nq].  O and O_p
+ *    have the input dtype; LSE is always float32 and uses the natural log.
+ *  - Device pointers must be 16-byte aligned.  D is 64 or 128.  B*H <= 65535,
+ *    1 <= Nq, Nk <= 2^30, 1 <= P <= DITA_MAX_PARTITIONS.
+ *  - O_p is normalised by its own partition's softmax denominator (each row
+ *    is a convex combination of V_p's rows); the unnormalised output is
+ *    exp(LSE_p) * O_p.
+ *  - Attention is bidirectional (no mask) with softmax scale `scale`
+ *    (<= 0 selects 1/sqrt(D)).
+ *  - Non-finite inputs are not supported and not checked.
+ *  - A cache handle is not thread-safe; calls that share one must be
+ *    serialised by the caller.
+ */
+#ifndef DITA_H
+#define DITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DITA_MAX_PARTITIONS 64
+
+typedef enum {
+  DITA_OK = 0,
+  DITA_ERR_ARG = 1,    /* null pointer, or an integer argument out of range      */
+  DITA_ERR_SHAPE = 2,  /* unsupported shape (D, B*H, Nq, Nk, P)                  */
+  DITA_ERR_DTYPE = 3,  /* unknown dtype                                          */
+  DITA_ERR_STATE = 4,  /* reuse of a slot that holds no state                    */
+  DITA_ERR_ALIGN = 5,  /* a device pointer is not 16-byte aligned                */
+  DITA_ERR_HIP = 6,    /* a HIP runtime call failed; see dita_last_hip_error()   */
+  DITA_ERR_SIZE = 7    /* a caller buffer is smaller than required               */
+} dita_status;
+
+typedef enum { DITA_F32 = 0, DITA_BF16 = 1 } dita_dtype;
+
+/* Shape of one rank's attention problem. */
+typedef struct {
+  int32_t B;      /* batch                                   */
+  int32_t H;      /* heads                                   */
+  int32_t D;      /* head dimension: 64 or 128               */
+  int32_t dtype;  /* dita_dtype of Q, K, V, O                */
+  int64_t Nq;     /* query rows of the rank's partition      */
+  float scale;    /* softmax scale; <= 0 selects 1/sqrt(D)   */
+} dita_shape;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* dita_status_str(int status);
+
+/* The hipError_t of the most recent DITA_ERR_HIP on the calling thread (0 if none). */
+int dita_last_hip_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int dita_version(void);
+
+/*
+ * dita_attn_partial -- fresh attention state of Q against one K/V partition.
+ * Page section: State-Centric Parallel Runtime > State Composition (a state
+ * is an output plus its log-sum-exp).
+ *
+ *   S = scale * Q K^T;  LSE_p = ln sum_j exp(S_ij);  O_p = exp(S - LSE_p) V
+ *
+ * q      [in]  device, [B, H, Nq, D] dtype
+ * k, v   [in]  device, [B, H, nk, D] dtype
+ * nk     [in]  keys in the partition, >= 1
+ * o_p    [out] device, [B, H, Nq, D] dtype (may not alias q, k, v)
+ * lse_p  [out] device, [B, H, Nq] float32
+ * bf16 runs on MFMA with fp32 accumulation; f32 keeps every step in fp32.
+ */
+int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
+                      int64_t nk, void* o_p, float* lse_p, void* stream);
+
+/*
+ * dita_state_merge -- exact LSE-weighted composition of P attention states.
+ * Page section: State-Centric Parallel Runtime > State Composition
+ * (associative, commutative composition of states).
+ *
+ *   M = max_p LSE_p;  w_p = exp(LSE_p - M);  L = sum_p w_p
+ *   O = sum_p (w_p / L) O_p;  LSE = M + ln L
+ * A state whose LSE is -inf has weight 0; rows where every LSE_p is -inf
+ * produce O = 0 and LSE = -inf.
+ *
+ * P         [in]  1..DITA_MAX_PARTITIONS
+ * o_list    [in]  host array of P device pointers, each [B, H, Nq, D] dtype
+ * lse_list  [in]  host array of P device pointers, each [B, H, Nq] float32
+ * o, lse    [out] device, [B, H, Nq, D] dtype and [B, H, Nq] float32; they
+ *                 may alias none of the inputs
+ */
+int dita_state_merge(const dita_shape* shape, int P, const void* const* o_list,
+                     const float* const* lse_list, void* o, float* lse, void* stream);
+
+/*
+ * State cache -- device-resident per-partition (O_p, LSE_p) slots.
+ * Page section: State-Centric Parallel Runtime > State Composition (cache
+ * composed states instead of raw K/V) and > Pipeline Orchestration ("reuse"
+ * operations load cached states).
+ *
+ * The caller allocates `bytes >= dita_state_cache_bytes(shape, P)` of device
+ * memory (16-byte aligned; 256 recommended) and keeps it alive while the
+ * handle exists.  Slot p holds O_p ([B, H, Nq, D] dtype) followed by LSE_p
+ * ([B, H, Nq] float32), each at a 256-byte aligned offset.  Host metadata per
+ * slot: valid (0/1) and stamp (the step that last wrote it, -1 if never).
+ */
+typedef struct dita_state_cache dita_state_cache;
+
+/* Device bytes a cache of P slots needs; 0 if the shape or P is invalid. */
+size_t dita_state_cache_bytes(const dita_shape* shape, int P);
+
+/* Create a handle over `dev_buf`; all slots start invalid.  *out is set only on DITA_OK. */
+int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
+                          size_t bytes);
+
+/* Destroy a handle (NULL is accepted).  Never frees dev_buf. */
+int dita_state_cache_free(dita_state_cache* cache);
+
+/* Device addresses of slot p's O and LSE (either output pointer may be NULL). */
+int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse);
+
+/* Copy a state into slot p (stream-ordered copy kernel) and mark it valid with `step`. */
+int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const float* lse,
+                           int64_t step, void* stream);
+
+/* Copy slot p out to caller buffers.  DITA_ERR_STATE if the slot is invalid. */
+int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* lse, void* stream);
+
+/* Mark slot p invalid (p = -1: every slot).  Device memory is untouched. */
+int dita_state_cache_invalidate(dita_state_cache* cache, int p);
+
+/* Read slot p's metadata (either output pointer may be NULL). */
+int dita_state_cache_info(const dita_state_cache* cache, int p, int* valid, int64_t* stamp);
+
+/* Cache geometry: P, and the shape it was created with. */
+int dita_state_cache_shape(const dita_state_cache* cache, dita_shape* shape, int* P);
+
+/*
+ * Reuse-mask planner (host only, integer arithmetic, deterministic).
+ * Page section: 1. Anchor-Guided Selection Planner -- anchor steps recompute
+ * every partition; the local partition is always computed; the rest are
+ * computed or reused per the policy.  The page prints no selection formula;
+ * the policies are fixed schedules:
+ *   DITA_PLAN_DIST      fresh iff |p - q| <= radius
+ *   DITA_PLAN_KNEAREST  fresh iff p is among the k_nearest partitions closest
+ *                       to q, ordered by (|p - q|, p)
+ *   DITA_PLAN_RANDOM    one SplitMix64 stream per step, seeded with
+ *                       (seed << 32) ^ step; P draws for p = 0..P-1 in order;
+ *                       reuse iff the draw's top bit is 1
+ *   DITA_PLAN_RAMP      fresh iff |p - q| <= r(step), r linear from `radius`
+ *                       at step 0 to `radius_end` at total_steps-1, rounded
+ *                       half up, clamped outside the schedule
+ * Overrides (fresh): p == q; anchor_period > 0 and step % anchor_period == 0;
+ * a slot that is not valid in `cache` (when cache is non-NULL).
+ */
+enum { DITA_PLAN_DIST = 0, DITA_PLAN_KNEAREST = 1, DITA_PLAN_RANDOM = 2, DITA_PLAN_RAMP = 3 };
+
+typedef struct {
+  int32_t P;              /* partitions, 1..DITA_MAX_PARTITIONS        */
+  int32_t q;              /* the rank's local partition, 0..P-1        */
+  int32_t policy;         /* DITA_PLAN_*                               */
+  int32_t radius;         /* DIST radius; RAMP radius at step 0, >= 0  */
+  int32_t radius_end;     /* RAMP radius at the last step, >= 0        */
+  int32_t k_nearest;      /* KNEAREST count, >= 0                      */
+  int32_t anchor_period;  /* > 0: every anchor_period-th step is fresh */
+  int32_t total_steps;    /* RAMP schedule length, >= 1                */
+  uint64_t seed;          /* RANDOM seed                               */
+} dita_plan;
+
+/* reuse_out [out, host]: P bytes, 1 = reuse the cached state, 0 = compute fresh. */
+int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t step,
+                   uint8_t* reuse_out);
+
+/*
+ * dita_attn_step -- one rank-step of selective state reuse.
+ * Page sections: 1. Anchor-Guided Selection Planner (per-partition compute or
+ * reuse) and 2. State-Centric Parallel Runtime > State Composition.
+ *
+ * For every p with reuse_mask[p] == 0 the fresh state of Q against
+ * (k_list[p], v_list[p]) is written straight into cache slot p (one grouped
+ * launch for all fresh partitions) and the slot is stamped with `step`; slots
+ * with reuse_mask[p] == 1 are left as they are and must be valid.  Then all P
+ * slots are merged into (o, lse).  Shape and P come from the cache.
+ *
+ * q                [in]  device [B, H, Nq, D]
+ * k_list, v_list   [in]  host arrays of P device pointers, [B, H, nk_list[p], D];
+ *                        entries of reused partitions are not read (may be NULL)
+ * nk_list          [in]  host array of P key counts (>= 1 where fresh)
+ * reuse_mask       [in]  host array of P bytes (0 fresh, 1 reuse; other values rejected)
+ * o, lse           [out] device final output and LSE
+ * info             [in/out, nullable] step report; its `events` members, when
+ *                  non-NULL, are hipEvent_t handles recorded on `stream` at the
+ *                  step start, after the fresh-attention launch and at the end.
+ */
+typedef struct {
+  int32_t n_fresh;       /* [out] partitions computed fresh             */
+  int32_t n_reused;      /* [out] partitions reused                     */
+  double fresh_flops;    /* [out] 4*B*H*Nq*sum(nk of fresh)*D           */
+  double merge_bytes;    /* [out] (P+1) * bytes of one state            */
+  void* ev_begin;        /* [in] hipEvent_t or NULL                     */
+  void* ev_attn_end;     /* [in] hipEvent_t or NULL                     */
+  void* ev_end;          /* [in] hipEvent_t or NULL                     */
+} dita_step_info;
+
+int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
+                   const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
+                   int64_t step, void* o, float* lse, void* stream, dita_step_info* info);
+
+/*
+ * Timing helpers (thin wrappers over HIP events, for benchmarks that time the
+ * kernels on the stream they run on).
+ */
+int dita_event_create(void** event);
+int dita_event_destroy(void* event);
+int dita_event_record(void* event, void* stream);
+/* Milliseconds between two recorded events; blocks until `stop` completes. */
+int dita_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITA_H */

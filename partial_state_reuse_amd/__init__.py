@@ -1,0 +1,358 @@
+"""Python binding of libdita: selective attention-state reuse on MI355X.
+
+Argument marshalling only.  Every step of the hot path runs in the HIP
+library (``libdita.so``, built in-tree by ``partial_state_reuse_amd.build``);
+PyTorch only supplies device memory and the current stream.  Importing this
+package fails loudly when the library has not been built: there is no
+fallback of any kind.
+
+The functions carry the names of the C entry points declared in
+``include/dita.h``:
+
+    dita_attn_partial   fresh attention state (O_p, LSE_p) of Q against one K/V partition
+    dita_state_merge    exact LSE-weighted merge of P states
+    dita_state_cache_*  device-resident per-partition state store (``StateCache`` wraps them)
+    dita_plan_mask      host reuse-mask planner
+    dita_attn_step      one compute-or-reuse rank-step over all P partitions
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdita.so")
+
+DITA_OK, DITA_ERR_ARG, DITA_ERR_SHAPE, DITA_ERR_DTYPE = 0, 1, 2, 3
+DITA_ERR_STATE, DITA_ERR_ALIGN, DITA_ERR_HIP, DITA_ERR_SIZE = 4, 5, 6, 7
+DITA_F32, DITA_BF16 = 0, 1
+DITA_PLAN_DIST, DITA_PLAN_KNEAREST, DITA_PLAN_RANDOM, DITA_PLAN_RAMP = 0, 1, 2, 3
+MAX_PARTITIONS = 64
+
+
+class DitaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {_lib.dita_status_str(status).decode()} (status {status})"
+        if status == DITA_ERR_HIP:
+            msg += f", hipError {_lib.dita_last_hip_error()}"
+        super().__init__(msg)
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("Nq", ctypes.c_int64), ("scale", ctypes.c_float)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("P", ctypes.c_int32), ("q", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("radius", ctypes.c_int32), ("radius_end", ctypes.c_int32),
+                ("k_nearest", ctypes.c_int32), ("anchor_period", ctypes.c_int32),
+                ("total_steps", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class StepInfo(ctypes.Structure):
+    _fields_ = [("n_fresh", ctypes.c_int32), ("n_reused", ctypes.c_int32),
+                ("fresh_flops", ctypes.c_double), ("merge_bytes", ctypes.c_double),
+                ("ev_begin", ctypes.c_void_p), ("ev_attn_end", ctypes.c_void_p),
+                ("ev_end", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    # torch must bring in its HIP runtime first: libdita then binds to that same runtime
+    # (both carry the soname libamdhip64.so.7).  Loaded the other way round, torch would
+    # load a second HIP runtime into the process.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m partial_state_reuse_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    pvp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "dita_status_str": (ctypes.c_char_p, [i32]),
+        "dita_last_hip_error": (i32, []),
+        "dita_version": (i32, []),
+        "dita_attn_partial": (i32, [ctypes.POINTER(Shape), vp, vp, vp, i64, vp, vp, vp]),
+        "dita_state_merge": (i32, [ctypes.POINTER(Shape), i32, pvp, pvp, vp, vp, vp]),
+        "dita_state_cache_bytes": (sz, [ctypes.POINTER(Shape), i32]),
+        "dita_state_cache_init": (i32, [pvp, ctypes.POINTER(Shape), i32, vp, sz]),
+        "dita_state_cache_free": (i32, [vp]),
+        "dita_state_cache_slot": (i32, [vp, i32, pvp, pvp]),
+        "dita_state_cache_store": (i32, [vp, i32, vp, vp, i64, vp]),
+        "dita_state_cache_load": (i32, [vp, i32, vp, vp, vp]),
+        "dita_state_cache_invalidate": (i32, [vp, i32]),
+        "dita_state_cache_info": (i32, [vp, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(i64)]),
+        "dita_state_cache_shape": (i32, [vp, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int)]),
+        "dita_plan_mask": (i32, [ctypes.POINTER(Plan), vp, i64, ctypes.POINTER(ctypes.c_uint8)]),
+        "dita_attn_step": (i32, [vp, vp, pvp, pvp, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_uint8),
+                                 i64, vp, vp, vp, ctypes.POINTER(StepInfo)]),
+        "dita_event_create": (i32, [pvp]),
+        "dita_event_destroy": (i32, [vp]),
+        "dita_event_record": (i32, [vp, vp]),
+        "dita_event_elapsed_ms": (i32, [vp, vp, ctypes.POINTER(ctypes.c_float)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (for symbol checks and raw calls)."""
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != DITA_OK:
+        raise DitaError(status, where)
+
+
+# --------------------------------------------------------------------------- marshalling
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DITA_BF16
+    if t.dtype == torch.float32:
+        return DITA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t, stream=None) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream
+
+
+def make_shape(q, scale: float = 0.0) -> Shape:
+    """Shape record of a [B, H, Nq, D] query tensor."""
+    B, H, Nq, D = q.shape
+    return Shape(B, H, D, _dtype_code(q), Nq, float(scale))
+
+
+def _ptr_array(ptrs: Sequence[Optional[int]]):
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+# --------------------------------------------------------------------------- entry points
+
+
+def dita_attn_partial(q, k, v, o=None, lse=None, scale: float = 0.0, stream=None):
+    """Fresh state (O_p, LSE_p) of ``q`` [B,H,Nq,D] against one partition ``k``, ``v`` [B,H,Nk,D]."""
+    torch = _torch()
+    if k.shape[:2] != q.shape[:2] or v.shape != k.shape or k.shape[3] != q.shape[3]:
+        raise ValueError("q, k, v shapes disagree")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    B, H, Nq, D = q.shape
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    shape = make_shape(q, scale)
+    _check(_lib.dita_attn_partial(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
+                                  _ptr(o), _ptr(lse), _stream(q, stream)), "dita_attn_partial")
+    return o, lse
+
+
+def dita_state_merge(o_list: Sequence, lse_list: Sequence, o=None, lse=None, scale: float = 0.0,
+                     stream=None):
+    """Merge P states (lists of [B,H,Nq,D] outputs and [B,H,Nq] fp32 LSEs)."""
+    torch = _torch()
+    if len(o_list) != len(lse_list) or not o_list:
+        raise ValueError("need equally long, non-empty state lists")
+    ref = o_list[0]
+    if o is None:
+        o = torch.empty_like(ref)
+    if lse is None:
+        lse = torch.empty(ref.shape[:3], dtype=torch.float32, device=ref.device)
+    shape = make_shape(ref, scale)
+    for x in o_list:
+        if x.shape != ref.shape or x.dtype != ref.dtype:
+            raise ValueError("state outputs must share shape and dtype")
+    for x in lse_list:
+        if x.shape != ref.shape[:3] or x.dtype != torch.float32:
+            raise ValueError("LSE arrays must be float32 [B, H, Nq]")
+    P = len(o_list)
+    _check(_lib.dita_state_merge(ctypes.byref(shape), P, _ptr_array([_ptr(x) for x in o_list]),
+                                 _ptr_array([_ptr(x) for x in lse_list]), _ptr(o), _ptr(lse),
+                                 _stream(ref, stream)), "dita_state_merge")
+    return o, lse
+
+
+def dita_plan_mask(plan: Plan, step: int, cache: Optional["StateCache"] = None) -> np.ndarray:
+    """Host reuse mask (uint8[P], 1 = reuse) from the library's planner."""
+    out = (ctypes.c_uint8 * plan.P)()
+    _check(_lib.dita_plan_mask(ctypes.byref(plan), cache.handle if cache else None, step, out),
+           "dita_plan_mask")
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+class StateCache:
+    """Device-resident (O_p, LSE_p) slots (the dita_state_cache_* calls).
+
+    The device buffer is a torch uint8 tensor owned by this object; the C
+    handle only records its address.
+    """
+
+    def __init__(self, B: int, H: int, Nq: int, D: int, dtype, P: int, device="cuda",
+                 scale: float = 0.0):
+        torch = _torch()
+        code = DITA_BF16 if dtype == torch.bfloat16 else DITA_F32 if dtype == torch.float32 else None
+        if code is None:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.shape = Shape(B, H, D, code, Nq, float(scale))
+        self.P = P
+        self.dtype = dtype
+        nbytes = _lib.dita_state_cache_bytes(ctypes.byref(self.shape), P)
+        if nbytes == 0:
+            raise ValueError("invalid cache shape or P")
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        _check(_lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(self.shape), P,
+                                          self.buffer.data_ptr(), nbytes), "dita_state_cache_init")
+        self.handle = h.value
+        self._views = [self._slot_views(p) for p in range(P)]
+
+    def _slot_views(self, p: int):
+        torch = _torch()
+        o_ptr, l_ptr = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(_lib.dita_state_cache_slot(self.handle, p, ctypes.byref(o_ptr), ctypes.byref(l_ptr)),
+               "dita_state_cache_slot")
+        s = self.shape
+        base = self.buffer.data_ptr()
+        esz = 2 if s.dtype == DITA_BF16 else 4
+        n = s.B * s.H * s.Nq
+        o = self.buffer[o_ptr.value - base: o_ptr.value - base + n * s.D * esz]
+        lse = self.buffer[l_ptr.value - base: l_ptr.value - base + n * 4]
+        return (o.view(self.dtype).view(s.B, s.H, s.Nq, s.D),
+                lse.view(torch.float32).view(s.B, s.H, s.Nq))
+
+    def slot(self, p: int):
+        """Views (O_p, LSE_p) of slot p's device memory."""
+        return self._views[p]
+
+    def store(self, p: int, o, lse, step: int, stream=None):
+        _check(_lib.dita_state_cache_store(self.handle, p, _ptr(o), _ptr(lse), step,
+                                           _stream(o, stream)), "dita_state_cache_store")
+
+    def load(self, p: int, o=None, lse=None, stream=None):
+        torch = _torch()
+        s = self.shape
+        if o is None:
+            o = torch.empty((s.B, s.H, s.Nq, s.D), dtype=self.dtype, device=self.buffer.device)
+        if lse is None:
+            lse = torch.empty((s.B, s.H, s.Nq), dtype=torch.float32, device=self.buffer.device)
+        _check(_lib.dita_state_cache_load(self.handle, p, _ptr(o), _ptr(lse), _stream(o, stream)),
+               "dita_state_cache_load")
+        return o, lse
+
+    def invalidate(self, p: int = -1):
+        _check(_lib.dita_state_cache_invalidate(self.handle, p), "dita_state_cache_invalidate")
+
+    def info(self, p: int):
+        valid, stamp = ctypes.c_int(), ctypes.c_int64()
+        _check(_lib.dita_state_cache_info(self.handle, p, ctypes.byref(valid), ctypes.byref(stamp)),
+               "dita_state_cache_info")
+        return bool(valid.value), stamp.value
+
+    def valid_mask(self) -> np.ndarray:
+        return np.array([self.info(p)[0] for p in range(self.P)], dtype=np.uint8)
+
+    def close(self):
+        if self.handle:
+            _lib.dita_state_cache_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reuse_mask,
+                   step: int, o=None, lse=None, stream=None, events=None) -> StepInfo:
+    """One rank-step: fresh states into their slots, reused slots kept, all P merged.
+
+    ``k_list``/``v_list`` hold P tensors [B,H,Nk_p,D] (entries of reused partitions may
+    be None).  ``events``: optional (begin, attn_end, end) raw hipEvent_t handles.
+    Returns (o, lse, StepInfo).
+    """
+    torch = _torch()
+    P = cache.P
+    if len(k_list) != P or len(v_list) != P:
+        raise ValueError("need P key and value tensors")
+    mask = np.ascontiguousarray(np.asarray(reuse_mask, dtype=np.uint8))
+    if mask.shape != (P,):
+        raise ValueError("reuse mask must have P entries")
+    s = cache.shape
+    if o is None:
+        o = torch.empty((s.B, s.H, s.Nq, s.D), dtype=cache.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((s.B, s.H, s.Nq), dtype=torch.float32, device=q.device)
+    nk = (ctypes.c_int64 * P)(*[(k.shape[2] if k is not None else 0) for k in k_list])
+    info = StepInfo()
+    if events is not None:
+        info.ev_begin, info.ev_attn_end, info.ev_end = events
+    m = (ctypes.c_uint8 * P).from_buffer_copy(mask.tobytes())
+    _check(_lib.dita_attn_step(cache.handle, _ptr(q), _ptr_array([_ptr(k) for k in k_list]),
+                               _ptr_array([_ptr(v) for v in v_list]), nk, m, step, _ptr(o),
+                               _ptr(lse), _stream(q, stream), ctypes.byref(info)), "dita_attn_step")
+    return o, lse, info
+
+
+class Event:
+    """A raw HIP event (for timing kernels on the stream they run on)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(_lib.dita_event_create(ctypes.byref(h)), "dita_event_create")
+        self.handle = h.value
+
+    def record(self, stream=None):
+        torch = _torch()
+        st = (stream or torch.cuda.current_stream()).cuda_stream
+        _check(_lib.dita_event_record(self.handle, st), "dita_event_record")
+
+    def elapsed_ms(self, later: "Event") -> float:
+        ms = ctypes.c_float()
+        _check(_lib.dita_event_elapsed_ms(self.handle, later.handle, ctypes.byref(ms)),
+               "dita_event_elapsed_ms")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _lib.dita_event_destroy(self.handle)
+        except Exception:
+            pass

@@ -1,0 +1,359 @@
+// C ABI: argument validation, the state-cache handle, and rank-step dispatch.
+//
+// Every entry point validates all of its arguments before it makes any HIP
+// call, so a rejected call launches nothing and changes nothing.  Launches are
+// asynchronous on the caller's stream; the library never synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/dita.h"
+#include "dita_kernels.h"
+#include "planner.h"
+
+struct dita_state_cache {
+  dita_shape shape;
+  int P;
+  char* base;
+  size_t bytes;
+  size_t o_bytes;      // bytes of one slot's O
+  size_t lse_offset;   // offset of LSE inside a slot
+  size_t slot_stride;  // bytes per slot
+  uint8_t valid[DITA_MAX_PARTITIONS];
+  int64_t stamp[DITA_MAX_PARTITIONS];
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return DITA_OK;
+  g_last_hip_error = int(e);
+  return DITA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_size(int dtype) { return dtype == DITA_BF16 ? 2 : 4; }
+
+int check_shape(const dita_shape* s) {
+  if (!s) return DITA_ERR_ARG;
+  if (s->dtype != DITA_F32 && s->dtype != DITA_BF16) return DITA_ERR_DTYPE;
+  if (s->B < 1 || s->H < 1 || int64_t(s->B) * s->H > 65535) return DITA_ERR_SHAPE;
+  if (s->D != 64 && s->D != 128) return DITA_ERR_SHAPE;
+  if (s->Nq < 1 || s->Nq > kMaxRows) return DITA_ERR_SHAPE;
+  if (std::isnan(s->scale) || std::isinf(s->scale)) return DITA_ERR_ARG;
+  return DITA_OK;
+}
+
+int check_dev(const void* p) {
+  if (!p) return DITA_ERR_ARG;
+  return aligned16(p) ? DITA_OK : DITA_ERR_ALIGN;
+}
+
+float eff_scale(const dita_shape& s) { return s.scale > 0.0f ? s.scale : 1.0f / std::sqrt(float(s.D)); }
+
+size_t state_o_bytes(const dita_shape& s) {
+  return size_t(s.B) * size_t(s.H) * size_t(s.Nq) * size_t(s.D) * elem_size(s.dtype);
+}
+size_t state_lse_bytes(const dita_shape& s) { return size_t(s.B) * size_t(s.H) * size_t(s.Nq) * 4; }
+
+dita::AttnProblem problem(const dita_shape& s) {
+  dita::AttnProblem pr;
+  pr.BH = s.B * s.H;
+  pr.D = s.D;
+  pr.Nq = s.Nq;
+  pr.scale = eff_scale(s);
+  return pr;
+}
+
+hipError_t launch_attn(const dita_shape& s, const void* q, const dita::AttnJobs& jobs, int n,
+                       hipStream_t st) {
+  const dita::AttnProblem pr = problem(s);
+  return s.dtype == DITA_BF16 ? dita::launch_attn_bf16(pr, q, jobs, n, st)
+                              : dita::launch_attn_f32(pr, q, jobs, n, st);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_slot(const dita_state_cache* c, int p) {
+  if (!c) return DITA_ERR_ARG;
+  if (p < 0 || p >= c->P) return DITA_ERR_ARG;
+  return DITA_OK;
+}
+
+void* slot_o(const dita_state_cache* c, int p) { return c->base + size_t(p) * c->slot_stride; }
+float* slot_lse(const dita_state_cache* c, int p) {
+  return reinterpret_cast<float*>(c->base + size_t(p) * c->slot_stride + c->lse_offset);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dita_status_str(int status) {
+  switch (status) {
+    case DITA_OK: return "ok";
+    case DITA_ERR_ARG: return "invalid argument";
+    case DITA_ERR_SHAPE: return "unsupported shape";
+    case DITA_ERR_DTYPE: return "unsupported dtype";
+    case DITA_ERR_STATE: return "reuse of a cache slot that holds no state";
+    case DITA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case DITA_ERR_HIP: return "HIP runtime error";
+    case DITA_ERR_SIZE: return "buffer too small";
+    default: return "unknown status";
+  }
+}
+
+int dita_last_hip_error(void) { return g_last_hip_error; }
+
+int dita_version(void) { return 100; }
+
+int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
+                      int64_t nk, void* o_p, float* lse_p, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  for (const void* p : {q, k, v, static_cast<const void*>(o_p), static_cast<const void*>(lse_p)})
+    if ((st = check_dev(p))) return st;
+  if (nk < 1 || nk > kMaxRows) return DITA_ERR_SHAPE;
+  dita::AttnJobs jobs;
+  jobs.job[0] = dita::AttnJob{k, v, o_p, lse_p, nk};
+  return hip_status(launch_attn(*shape, q, jobs, 1, static_cast<hipStream_t>(stream)));
+}
+
+int dita_state_merge(const dita_shape* shape, int P, const void* const* o_list,
+                     const float* const* lse_list, void* o, float* lse, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if (!o_list || !lse_list) return DITA_ERR_ARG;
+  if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
+  const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
+  dita::MergeSrc src;
+  for (int p = 0; p < P; ++p) {
+    if ((st = check_dev(o_list[p])) || (st = check_dev(lse_list[p]))) return st;
+    if (overlaps(o_list[p], ob, o, ob) || overlaps(lse_list[p], lb, lse, lb) ||
+        overlaps(o_list[p], ob, lse, lb) || overlaps(lse_list[p], lb, o, ob))
+      return DITA_ERR_ARG;
+    src.o[p] = o_list[p];
+    src.lse[p] = lse_list[p];
+  }
+  const int64_t rows = int64_t(shape->B) * shape->H * shape->Nq;
+  return hip_status(dita::launch_merge(shape->dtype, shape->D, rows, P, src, o, lse,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t dita_state_cache_bytes(const dita_shape* shape, int P) {
+  if (check_shape(shape) || P < 1 || P > DITA_MAX_PARTITIONS) return 0;
+  return size_t(P) * (align256(state_o_bytes(*shape)) + align256(state_lse_bytes(*shape)));
+}
+
+int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
+                          size_t bytes) {
+  if (!out) return DITA_ERR_ARG;
+  int st = check_shape(shape);
+  if (st) return st;
+  if (P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if ((st = check_dev(dev_buf))) return st;
+  const size_t need = dita_state_cache_bytes(shape, P);
+  if (bytes < need) return DITA_ERR_SIZE;
+  dita_state_cache* c = new (std::nothrow) dita_state_cache;
+  if (!c) return DITA_ERR_ARG;
+  c->shape = *shape;
+  c->P = P;
+  c->base = static_cast<char*>(dev_buf);
+  c->bytes = bytes;
+  c->o_bytes = state_o_bytes(*shape);
+  c->lse_offset = align256(c->o_bytes);
+  c->slot_stride = c->lse_offset + align256(state_lse_bytes(*shape));
+  std::memset(c->valid, 0, sizeof(c->valid));
+  for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) c->stamp[p] = -1;
+  *out = c;
+  return DITA_OK;
+}
+
+int dita_state_cache_free(dita_state_cache* cache) {
+  delete cache;
+  return DITA_OK;
+}
+
+int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse) {
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  if (o) *o = slot_o(cache, p);
+  if (lse) *lse = slot_lse(cache, p);
+  return DITA_OK;
+}
+
+int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const float* lse,
+                           int64_t step, void* stream) {
+  int st = check_slot(cache, p);
+  if (st) return st;
+  if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
+  if (step < 0) return DITA_ERR_ARG;
+  const size_t lb = state_lse_bytes(cache->shape);
+  if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
+      overlaps(lse, lb, cache->base, cache->bytes))
+    return DITA_ERR_ARG;
+  st = hip_status(dita::launch_copy_state(o, lse, slot_o(cache, p), slot_lse(cache, p),
+                                          cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
+  if (st) return st;
+  cache->valid[p] = 1;
+  cache->stamp[p] = step;
+  return DITA_OK;
+}
+
+int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* lse, void* stream) {
+  int st = check_slot(cache, p);
+  if (st) return st;
+  if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
+  if (!cache->valid[p]) return DITA_ERR_STATE;
+  const size_t lb = state_lse_bytes(cache->shape);
+  if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
+      overlaps(lse, lb, cache->base, cache->bytes))
+    return DITA_ERR_ARG;
+  return hip_status(dita::launch_copy_state(slot_o(cache, p), slot_lse(cache, p), o, lse,
+                                            cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
+}
+
+int dita_state_cache_invalidate(dita_state_cache* cache, int p) {
+  if (!cache) return DITA_ERR_ARG;
+  if (p == -1) {
+    for (int i = 0; i < cache->P; ++i) {
+      cache->valid[i] = 0;
+      cache->stamp[i] = -1;
+    }
+    return DITA_OK;
+  }
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  cache->valid[p] = 0;
+  cache->stamp[p] = -1;
+  return DITA_OK;
+}
+
+int dita_state_cache_info(const dita_state_cache* cache, int p, int* valid, int64_t* stamp) {
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  if (valid) *valid = cache->valid[p];
+  if (stamp) *stamp = cache->stamp[p];
+  return DITA_OK;
+}
+
+int dita_state_cache_shape(const dita_state_cache* cache, dita_shape* shape, int* P) {
+  if (!cache) return DITA_ERR_ARG;
+  if (shape) *shape = cache->shape;
+  if (P) *P = cache->P;
+  return DITA_OK;
+}
+
+int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t step,
+                   uint8_t* reuse_out) {
+  if (!plan || !reuse_out || step < 0) return DITA_ERR_ARG;
+  if (!dita::plan_valid(*plan)) return DITA_ERR_ARG;
+  if (cache && cache->P != plan->P) return DITA_ERR_ARG;
+  dita::plan_mask(*plan, step, cache ? cache->valid : nullptr, reuse_out);
+  return DITA_OK;
+}
+
+int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
+                   const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
+                   int64_t step, void* o, float* lse, void* stream, dita_step_info* info) {
+  if (!cache || !k_list || !v_list || !nk_list || !reuse_mask) return DITA_ERR_ARG;
+  int st;
+  if ((st = check_dev(q)) || (st = check_dev(o)) || (st = check_dev(lse))) return st;
+  if (step < 0) return DITA_ERR_ARG;
+  const dita_shape& s = cache->shape;
+  const int P = cache->P;
+  const size_t ob = cache->o_bytes, lb = state_lse_bytes(s);
+  if (overlaps(o, ob, cache->base, cache->bytes) || overlaps(lse, lb, cache->base, cache->bytes) ||
+      overlaps(q, ob, cache->base, cache->bytes) || overlaps(o, ob, lse, lb))
+    return DITA_ERR_ARG;
+
+  dita::AttnJobs jobs;
+  int n_fresh = 0;
+  double fresh_keys = 0.0;
+  for (int p = 0; p < P; ++p) {
+    if (reuse_mask[p] > 1) return DITA_ERR_ARG;
+    if (reuse_mask[p]) {
+      if (!cache->valid[p]) return DITA_ERR_STATE;
+      continue;
+    }
+    if ((st = check_dev(k_list[p])) || (st = check_dev(v_list[p]))) return st;
+    if (nk_list[p] < 1 || nk_list[p] > kMaxRows) return DITA_ERR_SHAPE;
+    jobs.job[n_fresh++] = dita::AttnJob{k_list[p], v_list[p], slot_o(cache, p), slot_lse(cache, p),
+                                        nk_list[p]};
+    fresh_keys += double(nk_list[p]);
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (info && info->ev_begin && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_begin), hs))))
+    return st;
+  if (n_fresh > 0 && (st = hip_status(launch_attn(s, q, jobs, n_fresh, hs)))) return st;
+  if (info && info->ev_attn_end &&
+      (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_attn_end), hs))))
+    return st;
+  for (int p = 0; p < P; ++p)
+    if (!reuse_mask[p]) {
+      cache->valid[p] = 1;
+      cache->stamp[p] = step;
+    }
+
+  dita::MergeSrc src;
+  for (int p = 0; p < P; ++p) {
+    src.o[p] = slot_o(cache, p);
+    src.lse[p] = slot_lse(cache, p);
+  }
+  const int64_t rows = int64_t(s.B) * s.H * s.Nq;
+  if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, P, src, o, lse, hs)))) return st;
+  if (info && info->ev_end && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_end), hs))))
+    return st;
+  if (info) {
+    info->n_fresh = n_fresh;
+    info->n_reused = P - n_fresh;
+    info->fresh_flops = 4.0 * double(s.B) * s.H * double(s.Nq) * fresh_keys * s.D;
+    info->merge_bytes = double(P + 1) * double(ob + lb);
+  }
+  return DITA_OK;
+}
+
+int dita_event_create(void** event) {
+  if (!event) return DITA_ERR_ARG;
+  hipEvent_t e = nullptr;
+  const int st = hip_status(hipEventCreate(&e));
+  if (st) return st;
+  *event = e;
+  return DITA_OK;
+}
+
+int dita_event_destroy(void* event) {
+  if (!event) return DITA_OK;
+  return hip_status(hipEventDestroy(static_cast<hipEvent_t>(event)));
+}
+
+int dita_event_record(void* event, void* stream) {
+  if (!event) return DITA_ERR_ARG;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)));
+}
+
+int dita_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return DITA_ERR_ARG;
+  int st = hip_status(hipEventSynchronize(static_cast<hipEvent_t>(stop)));
+  if (st) return st;
+  return hip_status(
+      hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (api.hip) and the device kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dita {
+
+constexpr int kMaxParts = 64;
+
+// One fresh (query partition, KV partition) block of a grouped attention launch.
+struct AttnJob {
+  const void* k;   // [B, H, nk, D]
+  const void* v;   // [B, H, nk, D]
+  void* o;         // [B, H, Nq, D]
+  float* lse;      // [B, H, Nq]
+  int64_t nk;
+};
+
+struct AttnJobs {
+  AttnJob job[kMaxParts];
+};
+
+struct AttnProblem {
+  int BH;          // B * H
+  int D;           // 64 or 128
+  int64_t Nq;
+  float scale;     // softmax scale (> 0)
+};
+
+// bf16 Q/K/V/O, MFMA with fp32 accumulation.  Launches grid.z = n_jobs.
+hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
+                            hipStream_t stream);
+// fp32 throughout.
+hipError_t launch_attn_f32(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
+                           hipStream_t stream);
+
+struct MergeSrc {
+  const void* o[kMaxParts];
+  const float* lse[kMaxParts];
+};
+
+// P-way LSE merge over `rows` = B*H*Nq rows of D elements.  dtype: 0 fp32, 1 bf16.
+hipError_t launch_merge(int dtype, int D, int64_t rows, int P, const MergeSrc& src, void* o,
+                        float* lse, hipStream_t stream);
+
+// Copy of one attention state (O bytes and LSE bytes, each a multiple of 4 bytes).
+hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,
+                             size_t o_bytes, size_t lse_bytes, hipStream_t stream);
+
+}  // namespace dita

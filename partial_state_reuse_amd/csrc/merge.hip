@@ -1,0 +1,171 @@
+// Exact LSE-weighted merge of P attention states, and the state copy kernel.
+//
+// Merge (the state composition of the DiTango page, State-Centric Parallel
+// Runtime > State Composition), per row:
+//     M = max_p LSE_p,  w_p = exp(LSE_p - M),  L = sum_p w_p,
+//     O = sum_p (w_p / L) O_p,  LSE = M + ln L
+// States with LSE = -inf weigh 0; a row whose every LSE is -inf becomes
+// (0, -inf).
+//
+// The pass is bound by HBM bandwidth: it reads P states and writes one,
+// (P+1) * (D * sizeof(dtype) + 4) bytes per row, and does ~2*P*D flops per
+// row.  A row is handled by D*sizeof(dtype)/16 lanes, each moving one
+// 16-byte chunk of every O_p (fully coalesced: consecutive lanes, consecutive
+// chunks, consecutive rows); eight partitions' chunks are in flight per lane
+// before any is consumed.  Accumulation is fp32.
+
+#include "dita_kernels.h"
+
+#include <cmath>
+
+namespace dita {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kInFlight = 8;
+
+template <typename T>
+struct Vec;
+
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(u32x4 r, float* x) {
+    // Element by value first: a bit_cast of a vector-element lvalue reads element 0.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = r[i];
+      x[i] = __builtin_bit_cast(float, u);
+    }
+  }
+  __device__ static u32x4 pack(const float* x) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, x[i]);
+    return r;
+  }
+};
+
+template <>
+struct Vec<__bf16> {
+  static constexpr int N = 8;
+  __device__ static void unpack(u32x4 r, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, r[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, r[i] & 0xffff0000u);
+    }
+  }
+  __device__ static u32x4 pack(const float* x) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)x[2 * i]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)x[2 * i + 1]);
+      r[i] = lo | (hi << 16);
+    }
+    return r;
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows,
+                                                         T* __restrict__ o, float* __restrict__ lse) {
+  constexpr int VN = Vec<T>::N;
+  constexpr int LPR = D / VN;          // lanes per row
+  constexpr int RPB = kThreads / LPR;  // rows per block
+  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  if (row >= rows) return;
+  const int64_t off = row * D + c * VN;
+
+  float M = -INFINITY;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, src.lse[p][row]);
+
+  float acc[VN];
+#pragma unroll
+  for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+  if (M == -INFINITY) {
+    *reinterpret_cast<u32x4*>(o + off) = Vec<T>::pack(acc);
+    if (c == 0) lse[row] = -INFINITY;
+    return;
+  }
+
+  float L = 0.0f;
+  for (int p0 = 0; p0 < P; p0 += kInFlight) {
+    u32x4 raw[kInFlight];
+    float lp[kInFlight];
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) {
+      if (p0 + j < P) {
+        raw[j] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(src.o[p0 + j]) + off);
+        lp[j] = src.lse[p0 + j][row];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) {
+      if (p0 + j < P) {
+        const float w = expf(lp[j] - M);  // 0 for LSE_p = -inf
+        L += w;
+        float x[VN];
+        Vec<T>::unpack(raw[j], x);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(w, x[i], acc[i]);
+      }
+    }
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < VN; ++i) acc[i] *= inv;
+  *reinterpret_cast<u32x4*>(o + off) = Vec<T>::pack(acc);
+  if (c == 0) lse[row] = M + logf(L);
+}
+
+template <typename T, int D>
+hipError_t launch_merge_t(int64_t rows, int P, const MergeSrc& src, void* o, float* lse,
+                          hipStream_t stream) {
+  constexpr int LPR = D / Vec<T>::N;
+  constexpr int RPB = kThreads / LPR;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  merge_kernel<T, D><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(src, P, rows,
+                                                                      static_cast<T*>(o), lse);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kThreads) void copy_state_kernel(const u32x4* __restrict__ so,
+                                                              u32x4* __restrict__ dO, int64_t n16,
+                                                              const float* __restrict__ sl,
+                                                              float* __restrict__ dl, int64_t n4) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride) dO[i] = so[i];
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n4; i += stride) dl[i] = sl[i];
+}
+
+}  // namespace
+
+hipError_t launch_merge(int dtype, int D, int64_t rows, int P, const MergeSrc& src, void* o,
+                        float* lse, hipStream_t stream) {
+  if (dtype == 1) {
+    return D == 128 ? launch_merge_t<__bf16, 128>(rows, P, src, o, lse, stream)
+                    : launch_merge_t<__bf16, 64>(rows, P, src, o, lse, stream);
+  }
+  return D == 128 ? launch_merge_t<float, 128>(rows, P, src, o, lse, stream)
+                  : launch_merge_t<float, 64>(rows, P, src, o, lse, stream);
+}
+
+hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,
+                             size_t o_bytes, size_t lse_bytes, hipStream_t stream) {
+  const int64_t n16 = int64_t(o_bytes / 16);
+  const int64_t n4 = int64_t(lse_bytes / 4);
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  copy_state_kernel<<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(
+      static_cast<const u32x4*>(src_o), static_cast<u32x4*>(dst_o), n16, src_lse, dst_lse, n4);
+  return hipGetLastError();
+}
+
+}  // namespace dita

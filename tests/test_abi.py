@@ -1,0 +1,227 @@
+"""C-ABI checks that need no GPU: exports, planner bit-parity, argument validation.
+
+Every call made here either touches host metadata only (the planner, the
+cache handle) or is rejected by validation before the library makes any HIP
+call, so nothing is launched.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import Plan as OraclePlan
+from oracle import plan_mask as oracle_plan_mask
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+dita = pytest.importorskip("partial_state_reuse_amd")
+lib = dita.lib()
+
+FAKE_DEV = 0x7F0000000000  # an aligned address that is never dereferenced here
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "dita.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dita_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert lib.dita_status_str(0) == b"ok"
+    assert b"align" in lib.dita_status_str(dita.DITA_ERR_ALIGN)
+    assert lib.dita_status_str(99) == b"unknown status"
+    assert lib.dita_version() >= 100
+
+
+def _lib_mask(plan: OraclePlan, step):
+    cp = dita.Plan(plan.P, plan.q, plan.policy, plan.radius, plan.radius_end, plan.k_nearest,
+                   plan.anchor_period, plan.total_steps, plan.seed)
+    out = (ctypes.c_uint8 * plan.P)()
+    assert lib.dita_plan_mask(ctypes.byref(cp), None, step, out) == 0
+    return np.frombuffer(bytes(out), np.uint8)
+
+
+def _cache(shape, P):
+    h = ctypes.c_void_p()
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), P)
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), P, FAKE_DEV, n) == 0
+    return h.value
+
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_planner_matches_oracle_on_workload_schedules(name):
+    wl = workloads.get(name)
+    plan = OraclePlan(**wl.plan_fields())
+    for s in range(wl.steps):
+        assert np.array_equal(_lib_mask(plan, s), oracle_plan_mask(plan, s)), (name, s)
+
+
+def test_planner_matches_oracle_on_random_plans():
+    rng = np.random.default_rng(1234)
+    for _ in range(10000):
+        P = int(rng.integers(1, 65))
+        plan = OraclePlan(P=P, q=int(rng.integers(0, P)), policy=int(rng.integers(0, 4)),
+                          radius=int(rng.integers(0, 70)), radius_end=int(rng.integers(0, 70)),
+                          k_nearest=int(rng.integers(0, P + 2)),
+                          anchor_period=int(rng.integers(0, 7)),
+                          total_steps=int(rng.integers(1, 100)),
+                          seed=int(rng.integers(0, 2**63)) * 2 + int(rng.integers(0, 2)))
+        s = int(rng.integers(0, 200))
+        assert np.array_equal(_lib_mask(plan, s), oracle_plan_mask(plan, s)), (plan, s)
+
+
+def test_planner_rejects_bad_plans():
+    out = (ctypes.c_uint8 * 64)()
+    for bad in [dita.Plan(0, 0, 0, 0, 0, 0, 0, 1, 0), dita.Plan(65, 0, 0, 0, 0, 0, 0, 1, 0),
+                dita.Plan(4, 4, 0, 0, 0, 0, 0, 1, 0), dita.Plan(4, 0, 9, 0, 0, 0, 0, 1, 0),
+                dita.Plan(4, 0, 0, -1, 0, 0, 0, 1, 0), dita.Plan(4, 0, 3, 0, 0, 0, 0, 0, 0),
+                dita.Plan(4, 0, 0, 0, 0, -2, 0, 1, 0), dita.Plan(4, 0, 0, 0, 0, 0, -1, 1, 0)]:
+        assert lib.dita_plan_mask(ctypes.byref(bad), None, 0, out) == dita.DITA_ERR_ARG
+    ok = dita.Plan(4, 0, 0, 0, 0, 0, 0, 1, 0)
+    assert lib.dita_plan_mask(ctypes.byref(ok), None, -1, out) == dita.DITA_ERR_ARG
+    assert lib.dita_plan_mask(ctypes.byref(ok), None, 0, None) == dita.DITA_ERR_ARG
+
+
+def test_cache_metadata_host_only():
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 100, 0.0)
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), 3)
+    o_bytes = 1 * 2 * 100 * 128 * 2
+    lse_bytes = 1 * 2 * 100 * 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert n == 3 * (align(o_bytes) + align(lse_bytes))
+    h = _cache(shape, 3)
+    o, l = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.dita_state_cache_slot(h, 2, ctypes.byref(o), ctypes.byref(l)) == 0
+    assert o.value == FAKE_DEV + 2 * (align(o_bytes) + align(lse_bytes))
+    assert l.value == o.value + align(o_bytes)
+    valid, stamp = ctypes.c_int(), ctypes.c_int64()
+    for p in range(3):
+        assert lib.dita_state_cache_info(h, p, ctypes.byref(valid), ctypes.byref(stamp)) == 0
+        assert valid.value == 0 and stamp.value == -1
+    assert lib.dita_state_cache_info(h, 3, None, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_invalidate(h, -1) == 0
+    assert lib.dita_state_cache_invalidate(h, 5) == dita.DITA_ERR_ARG
+    sh, P = dita.Shape(), ctypes.c_int()
+    assert lib.dita_state_cache_shape(h, ctypes.byref(sh), ctypes.byref(P)) == 0
+    assert (sh.B, sh.H, sh.D, sh.Nq, P.value) == (1, 2, 128, 100, 3)
+    # Loading an empty slot is a state error, detected before any copy is issued.
+    assert lib.dita_state_cache_load(h, 0, FAKE_DEV, FAKE_DEV + 4096, None) == dita.DITA_ERR_STATE
+    # The planner honours cold slots: with every slot empty, everything is fresh.
+    plan = dita.Plan(3, 0, dita.DITA_PLAN_DIST, 0, 0, 0, 0, 1, 0)
+    out = (ctypes.c_uint8 * 3)()
+    assert lib.dita_plan_mask(ctypes.byref(plan), h, 4, out) == 0
+    assert list(out) == [0, 0, 0]
+    plan4 = dita.Plan(4, 0, dita.DITA_PLAN_DIST, 0, 0, 0, 0, 1, 0)
+    assert lib.dita_plan_mask(ctypes.byref(plan4), h, 4, out) == dita.DITA_ERR_ARG  # P mismatch
+    lib.dita_state_cache_free(h)
+    assert lib.dita_state_cache_free(None) == 0
+
+
+def test_cache_init_validation():
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 100, 0.0)
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), 3)
+    h = ctypes.c_void_p()
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), 3, FAKE_DEV, n - 1) == dita.DITA_ERR_SIZE
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), 0, FAKE_DEV, n) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), 65, FAKE_DEV, n) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), 3, FAKE_DEV + 8, n) == dita.DITA_ERR_ALIGN
+    assert lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(shape), 3, None, n) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_init(None, ctypes.byref(shape), 3, FAKE_DEV, n) == dita.DITA_ERR_ARG
+    assert h.value is None
+    assert lib.dita_state_cache_bytes(None, 3) == 0
+    bad = dita.Shape(1, 2, 96, dita.DITA_BF16, 100, 0.0)
+    assert lib.dita_state_cache_bytes(ctypes.byref(bad), 3) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("D", 96, dita.DITA_ERR_SHAPE), ("D", 256, dita.DITA_ERR_SHAPE), ("B", 0, dita.DITA_ERR_SHAPE),
+    ("H", 70000, dita.DITA_ERR_SHAPE), ("Nq", 0, dita.DITA_ERR_SHAPE),
+    ("Nq", 2**31, dita.DITA_ERR_SHAPE), ("dtype", 5, dita.DITA_ERR_DTYPE),
+    ("scale", float("nan"), dita.DITA_ERR_ARG), ("scale", float("inf"), dita.DITA_ERR_ARG),
+])
+def test_attn_partial_rejects_bad_shape(field, value, status):
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    setattr(shape, field, value)
+    p = FAKE_DEV
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 64, p, p, None) == status
+
+
+def test_attn_partial_rejects_bad_pointers_and_nk():
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    p = FAKE_DEV
+    assert lib.dita_attn_partial(None, p, p, p, 64, p, p, None) == dita.DITA_ERR_ARG
+    assert lib.dita_attn_partial(ctypes.byref(shape), None, p, p, 64, p, p, None) == dita.DITA_ERR_ARG
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p + 2, p, 64, p, p, None) == dita.DITA_ERR_ALIGN
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 64, p, p + 4, None) == dita.DITA_ERR_ALIGN
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 0, p, p, None) == dita.DITA_ERR_SHAPE
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 2**31, p, p, None) == dita.DITA_ERR_SHAPE
+
+
+def test_state_merge_rejects_bad_arguments():
+    shape = dita.Shape(1, 2, 64, dita.DITA_F32, 64, 0.0)
+    p = FAKE_DEV
+    arr = lambda *x: (ctypes.c_void_p * len(x))(*x)
+    o_bytes = 2 * 64 * 64 * 4
+    srcs = arr(p, p + (1 << 20))
+    lses = arr(p + (2 << 20), p + (3 << 20))
+    out, out_l = p + (4 << 20), p + (5 << 20)
+    assert lib.dita_state_merge(ctypes.byref(shape), 0, srcs, lses, out, out_l, None) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_merge(ctypes.byref(shape), 65, srcs, lses, out, out_l, None) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_merge(ctypes.byref(shape), 2, None, lses, out, out_l, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_merge(ctypes.byref(shape), 2, arr(p, p + 8), lses, out, out_l, None) == dita.DITA_ERR_ALIGN
+    assert lib.dita_state_merge(ctypes.byref(shape), 2, arr(p, None), lses, out, out_l, None) == dita.DITA_ERR_ARG
+    # output aliasing an input state
+    assert lib.dita_state_merge(ctypes.byref(shape), 2, arr(p, p + (1 << 20)), lses, p + 256, out_l,
+                                None) == dita.DITA_ERR_ARG
+    assert o_bytes < (1 << 20)
+
+
+def test_attn_step_validation_before_launch():
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    h = _cache(shape, 4)
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), 4)
+    q, o, l = FAKE_DEV + n + 4096, FAKE_DEV + n + (1 << 20), FAKE_DEV + n + (2 << 20)
+    ks = (ctypes.c_void_p * 4)(*[FAKE_DEV + n + ((3 + i) << 20) for i in range(4)])
+    nk = (ctypes.c_int64 * 4)(64, 64, 64, 64)
+    mask = lambda *m: (ctypes.c_uint8 * 4)(*m)
+    info = dita.StepInfo()
+    # Reusing a slot that was never filled.
+    assert lib.dita_attn_step(h, q, ks, ks, nk, mask(0, 1, 0, 0), 0, o, l, None, ctypes.byref(info)) == dita.DITA_ERR_STATE
+    # Mask values other than 0/1.
+    assert lib.dita_attn_step(h, q, ks, ks, nk, mask(0, 2, 0, 0), 0, o, l, None, None) == dita.DITA_ERR_ARG
+    # Output inside the cache buffer.
+    assert lib.dita_attn_step(h, q, ks, ks, nk, mask(0, 0, 0, 0), 0, FAKE_DEV + 256, l, None, None) == dita.DITA_ERR_ARG
+    # Bad key count of a fresh partition.
+    bad_nk = (ctypes.c_int64 * 4)(64, 0, 64, 64)
+    assert lib.dita_attn_step(h, q, ks, ks, bad_nk, mask(0, 0, 0, 0), 0, o, l, None, None) == dita.DITA_ERR_SHAPE
+    # Misaligned K of a fresh partition.
+    bad_k = (ctypes.c_void_p * 4)(ks[0], ks[1] + 2, ks[2], ks[3])
+    assert lib.dita_attn_step(h, q, bad_k, ks, nk, mask(0, 0, 0, 0), 0, o, l, None, None) == dita.DITA_ERR_ALIGN
+    # Negative step, null handle, null lists.
+    assert lib.dita_attn_step(h, q, ks, ks, nk, mask(0, 0, 0, 0), -1, o, l, None, None) == dita.DITA_ERR_ARG
+    assert lib.dita_attn_step(None, q, ks, ks, nk, mask(0, 0, 0, 0), 0, o, l, None, None) == dita.DITA_ERR_ARG
+    assert lib.dita_attn_step(h, q, None, ks, nk, mask(0, 0, 0, 0), 0, o, l, None, None) == dita.DITA_ERR_ARG
+    # Nothing changed.
+    valid, stamp = ctypes.c_int(), ctypes.c_int64()
+    for p in range(4):
+        lib.dita_state_cache_info(h, p, ctypes.byref(valid), ctypes.byref(stamp))
+        assert valid.value == 0 and stamp.value == -1
+    lib.dita_state_cache_free(h)
+
+
+def test_event_helpers_validate():
+    assert lib.dita_event_create(None) == dita.DITA_ERR_ARG
+    assert lib.dita_event_record(None, None) == dita.DITA_ERR_ARG
+    assert lib.dita_event_elapsed_ms(None, None, None) == dita.DITA_ERR_ARG
+    assert lib.dita_event_destroy(None) == 0

@@ -1,0 +1,142 @@
+"""GPU parity of the individual entry points against the fp64 oracle.
+
+Sizes span several query and key tiles with ragged tails on both axes, both
+head dims, both dtypes.  Inputs are seeded; bf16 inputs are rounded once and
+the oracle consumes exactly those values.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import TOL, assert_state_close, max_abs, say, to_dev, to_host
+from oracle import merge_states, partial_state
+from workloads import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (5, 1), (77, 63), (128, 64), (129, 65), (300, 257), (256, 1000), (1, 700)]
+
+
+def _inputs(rng, B, H, nq, nk, D, dtype, scale=1.0):
+    # V ~ 0.5 N(0,1), the value scale of the video-DiT workloads: the absolute bf16
+    # bound on O (1e-2) presumes |O| below ~2, where bf16's half-ulp is <= 0.0039.
+    q = rng.standard_normal((B, H, nq, D)).astype(np.float32) * np.float32(scale)
+    k = rng.standard_normal((B, H, nk, D)).astype(np.float32) * np.float32(scale)
+    v = rng.standard_normal((B, H, nk, D)).astype(np.float32) * np.float32(0.5)
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("nq,nk", SHAPES)
+def test_attn_partial_matches_oracle(dev, dtype, D, nq, nk):
+    import partial_state_reuse_amd as dita
+    say(f"attn_partial dtype={dtype} D={D} nq={nq} nk={nk}")
+    rng = np.random.default_rng(nq * 7919 + nk * 31 + D)
+    q, k, v = _inputs(rng, 1, 2, nq, nk, D, dtype, scale=1.5)
+    o, lse = dita.dita_attn_partial(to_dev(q, dtype, dev), to_dev(k, dtype, dev), to_dev(v, dtype, dev))
+    o_ref, lse_ref = partial_state(q, k, v)
+    eo, el = assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "attn_partial")
+    say(f"  O err {eo:.2e}  LSE err {el:.2e}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_attn_partial_large_scores_and_batches(dev, D):
+    """Scores spanning ~+-60 (exercises the lazy rescale) with B=2, H=3, explicit scale."""
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(5 + D)
+    q, k, v = _inputs(rng, 2, 3, 200, 900, D, "bf16", scale=3.0)
+    # sort keys so that later tiles hold larger scores and the running max moves often
+    order = np.argsort((q[:, :, :1] @ np.swapaxes(k, -1, -2))[..., 0, :], axis=-1)
+    k = np.take_along_axis(k, order[..., None], axis=2)
+    v = np.take_along_axis(v, order[..., None], axis=2)
+    o, lse = dita.dita_attn_partial(to_dev(q, "bf16", dev), to_dev(k, "bf16", dev),
+                                    to_dev(v, "bf16", dev), scale=0.25)
+    o_ref, lse_ref = partial_state(q, k, v, scale=0.25)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "large scores")
+
+
+def test_attn_partial_is_deterministic(dev):
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(9)
+    q, k, v = _inputs(rng, 1, 4, 333, 777, 128, "bf16")
+    tq, tk, tv = to_dev(q, "bf16", dev), to_dev(k, "bf16", dev), to_dev(v, "bf16", dev)
+    o1, l1 = dita.dita_attn_partial(tq, tk, tv)
+    o2, l2 = dita.dita_attn_partial(tq, tk, tv)
+    assert bool((o1 == o2).all()) and bool((l1 == l2).all())
+
+
+def _states(rng, P, B, H, nq, D, dtype, neg_inf_slot=None):
+    os_, ls = [], []
+    for p in range(P):
+        o = rng.standard_normal((B, H, nq, D)).astype(np.float32)
+        l = (3.0 * rng.standard_normal((B, H, nq)) + 5.0).astype(np.float32)
+        if dtype == "bf16":
+            o = round_bf16(o)
+        if p == neg_inf_slot:
+            l[:] = -np.inf
+        os_.append(o)
+        ls.append(l)
+    return os_, ls
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 9, 16, 64])
+def test_state_merge_matches_oracle(dev, dtype, D, P):
+    import partial_state_reuse_amd as dita
+    say(f"merge dtype={dtype} D={D} P={P}")
+    rng = np.random.default_rng(P * 100 + D)
+    os_, ls = _states(rng, P, 1, 3, 37, D, dtype, neg_inf_slot=1 if P > 2 else None)
+    o, lse = dita.dita_state_merge([to_dev(x, dtype, dev) for x in os_],
+                                   [to_dev(x, "f32", dev) for x in ls])
+    o_ref, lse_ref = merge_states(list(zip(os_, ls)))
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, dtype, "merge")
+
+
+def test_state_merge_all_neutral_rows(dev):
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(3)
+    os_, ls = _states(rng, 3, 1, 1, 8, 64, "f32")
+    for l in ls:
+        l[0, 0, :4] = -np.inf
+    o, lse = dita.dita_state_merge([to_dev(x, "f32", dev) for x in os_],
+                                   [to_dev(x, "f32", dev) for x in ls])
+    o, lse = to_host(o), to_host(lse)
+    assert np.all(o[0, 0, :4] == 0) and np.all(np.isneginf(lse[0, 0, :4]))
+    o_ref, lse_ref = merge_states(list(zip(os_, ls)))
+    assert max_abs(o[0, 0, 4:], o_ref[0, 0, 4:]) <= 1e-5
+
+
+def test_state_merge_single_state_is_identity_bitwise(dev):
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(4)
+    os_, ls = _states(rng, 1, 1, 2, 50, 128, "bf16")
+    o, lse = dita.dita_state_merge([to_dev(os_[0], "bf16", dev)], [to_dev(ls[0], "f32", dev)])
+    assert np.array_equal(to_host(o), os_[0].astype(np.float64))
+    assert max_abs(to_host(lse), ls[0]) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cache_store_load_roundtrip_bitwise(dev, dtype):
+    import torch
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(6)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cache = dita.StateCache(1, 2, 77, 128, tdt, P=3, device=dev)
+    os_, ls = _states(rng, 3, 1, 2, 77, 128, dtype)
+    for p in range(3):
+        cache.store(p, to_dev(os_[p], dtype, dev), to_dev(ls[p], "f32", dev), step=10 + p)
+    for p in (2, 0, 1):
+        o, l = cache.load(p)
+        assert np.array_equal(to_host(o), os_[p].astype(np.float64))
+        assert np.array_equal(to_host(l), ls[p].astype(np.float64))
+        assert cache.info(p) == (True, 10 + p)
+        so, sl = cache.slot(p)
+        assert bool((so == o).all()) and bool((sl == l).all())
+    cache.invalidate(1)
+    assert cache.info(1) == (False, -1)
+    with pytest.raises(dita.DitaError):
+        cache.load(1)

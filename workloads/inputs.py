@@ -61,9 +61,13 @@ def grid_coords(grid: Tuple[int, int, int]) -> np.ndarray:
 
 
 def _features(rng: np.random.Generator, coords: np.ndarray, D: int) -> np.ndarray:
+    """[N, D] float32 random Fourier features; the phase is taken in float64, the cosine in float32."""
     omega = rng.standard_normal((D, 3)) / np.asarray(LENGTH_SCALES)[None, :]
     phase = rng.uniform(0.0, 2.0 * math.pi, size=D)
-    return math.sqrt(2.0 / D) * np.cos(coords @ omega.T + phase[None, :])
+    arg = (coords @ omega.T + phase[None, :]).astype(np.float32)
+    np.cos(arg, out=arg)
+    arg *= np.float32(math.sqrt(2.0 / D))
+    return arg
 
 
 def _workers(n_jobs: int) -> int:
@@ -114,14 +118,20 @@ class Inputs:
             self._v0[b, hi] = _rng(self.seed, _NOISE_V, b, h).standard_normal((wl.N, wl.D), np.float32)
             return
         coords = grid_coords(wl.grid)
-        a_qk = math.sqrt(8.0 * math.sqrt(wl.D))
+        a_qk = np.float32(math.sqrt(8.0 * math.sqrt(wl.D)))
+        nz = np.float32(wl.noise)
         phi = _features(_rng(self.seed, _FEAT_QK, b, h), coords, wl.D)
-        phi_v = _features(_rng(self.seed, _FEAT_V, b, h), coords, wl.D)
-        nz = wl.noise
-        self.q[b, hi] = (a_qk * phi[q0:q1]
-                         + nz * _rng(self.seed, _NOISE_Q, b, h).standard_normal((wl.Nq, wl.D)))
-        self._k0[b, hi] = a_qk * phi + nz * _rng(self.seed, _NOISE_K, b, h).standard_normal((wl.N, wl.D))
-        self._v0[b, hi] = phi_v + nz * _rng(self.seed, _NOISE_V, b, h).standard_normal((wl.N, wl.D))
+        phi *= a_qk
+        q = self.q[b, hi]
+        q[...] = phi[q0:q1]
+        q += nz * _rng(self.seed, _NOISE_Q, b, h).standard_normal((wl.Nq, wl.D), np.float32)
+        k = self._k0[b, hi]
+        k[...] = phi
+        del phi
+        k += nz * _rng(self.seed, _NOISE_K, b, h).standard_normal((wl.N, wl.D), np.float32)
+        v = self._v0[b, hi]
+        v[...] = _features(_rng(self.seed, _FEAT_V, b, h), coords, wl.D)
+        v += nz * _rng(self.seed, _NOISE_V, b, h).standard_normal((wl.N, wl.D), np.float32)
 
     def _narrow(self, x: np.ndarray) -> np.ndarray:
         return round_bf16(x) if self.wl.dtype == "bf16" else x
@@ -133,11 +143,13 @@ class Inputs:
 
     def _add_noise(self, kind_k: int, kind_v: int, scale: float, step: int,
                    k: np.ndarray, v: np.ndarray) -> None:
+        sc = np.float32(scale)
+
         def job(b, hi, h):
-            k[b, hi] += np.float32(scale) * _rng(self.seed, kind_k, b, h, step).standard_normal(
-                k.shape[2:], np.float32)
-            v[b, hi] += np.float32(scale) * _rng(self.seed, kind_v, b, h, step).standard_normal(
-                v.shape[2:], np.float32)
+            for x, kind in ((k, kind_k), (v, kind_v)):
+                e = _rng(self.seed, kind, b, h, step).standard_normal(x.shape[2:], np.float32)
+                e *= sc
+                x[b, hi] += e
         self._parallel(job)
 
     def kv(self, step: int) -> Tuple[np.ndarray, np.ndarray]:
