@@ -1,0 +1,244 @@
+"""Benchmark: rank-steps of selective attention-state reuse on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the host mask planner, the grouped fresh partial-attention launch that writes
+states into the cache, and the P-way LSE merge, all through the C ABI.
+
+Default workload: 75,600 tokens (21 frames x 45x80 patches), H=40, D=128,
+bf16, P=16 context partitions of 4725 tokens; the rank owns partition 0 and
+recomputes partitions within distance 2, with a full refresh (anchor) every
+5th step.  The K/V of all 10 steps of that schedule are generated up front
+and resident in HBM before the timed region; timed step i uses the inputs
+and mask of schedule step (warmup + i) mod 10.
+
+Prints ONE JSON line:  value = fresh-block attention TFLOP/s over the whole
+timed job (fresh-block flops / wall time of the K steps), ms_per_step, the
+roofline of the dominant kernel (the fresh-attention launch, timed with HIP
+events on its own stream), the merge's bandwidth, and the fp64 CPU oracle
+timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--seed S]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit75k_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    return ap.parse_args()
+
+
+def upload_parts(x: np.ndarray, wl, dev, tdt):
+    import torch
+    out = []
+    for p in range(wl.P):
+        a, b = wl.part_range(p)
+        out.append(torch.from_numpy(np.ascontiguousarray(x[:, :, a:b])).to(tdt).to(dev))
+    return out
+
+
+def cpu_baseline(inp, wl, budget_s: float):
+    """The fp64 oracle's rank-step, timed as it stands on the host cores, on a head
+    sample of a non-anchor step (fresh blocks + P-way merge)."""
+    from oracle import Plan, StateCache, attn_step, plan_mask
+    from workloads import split_parts
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    plan = Plan(**wl.plan_fields())
+    # The first step index whose mask is not all-fresh with every slot filled.
+    s = next(i for i in range(1, wl.steps + 1)
+             if plan_mask(plan, i % wl.steps, np.ones(wl.P, np.uint8)).any())
+    mask = plan_mask(plan, s % wl.steps, np.ones(wl.P, np.uint8))
+    k, v = inp.kv(s % wl.steps)
+    kp, vp = split_parts(k, wl), split_parts(v, wl)
+    rng = np.random.default_rng(0)
+    heads_done, elapsed, flops = 0, 0.0, 0.0
+    for h in range(wl.H):
+        cache = StateCache(wl.P)
+        for p in range(wl.P):   # reused slots: any state of the right shape (untimed)
+            cache.store(p, (rng.standard_normal((wl.B, 1, wl.Nq, wl.D)),
+                            rng.standard_normal((wl.B, 1, wl.Nq)) + 9.0), 0)
+        qh = inp.q[:, h:h + 1]
+        kh = [x[:, h:h + 1] for x in kp]
+        vh = [x[:, h:h + 1] for x in vp]
+        t0 = time.perf_counter()
+        _, _, nf = attn_step(cache, qh, kh, vh, mask, s)
+        elapsed += time.perf_counter() - t0
+        flops += 4.0 * wl.B * wl.Nq * wl.D * sum(wl.Nk for p in range(wl.P) if mask[p] == 0)
+        heads_done += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "ms_per_step": elapsed / heads_done * wl.H * 1e3,
+        "sample": (f"fp64 numpy oracle rank-step (schedule step {s % wl.steps}: "
+                   f"{int((mask == 0).sum())} fresh blocks + {wl.P}-way merge) on {heads_done} of "
+                   f"{wl.H} heads, {elapsed:.1f} s; ms_per_step extrapolated to all heads"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "design is described in DESIGN.md and not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import partial_state_reuse_amd as dita
+    import workloads
+    from workloads import Inputs
+
+    wl = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    n_sched = wl.steps
+    log(f"[bench] {wl.name}: B={wl.B} H={wl.H} D={wl.D} N={wl.N} P={wl.P} Nk={wl.Nk} "
+        f"dtype={wl.dtype}; generating {n_sched} steps of inputs")
+    t_gen = time.perf_counter()
+    inp = Inputs(wl, seed=args.seed)
+    q = torch.from_numpy(inp.q).to(tdt).to(dev)
+    kv = []
+    for s in range(n_sched):
+        k, v = inp.kv(s)
+        kv.append((upload_parts(k, wl, dev, tdt), upload_parts(v, wl, dev, tdt)))
+        log(f"[bench] inputs for schedule step {s} resident")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s")
+
+    cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
+    plan = dita.Plan(**wl.plan_fields())
+    o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
+    lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(step_index, events=None):
+        si = step_index % n_sched
+        mask = dita.dita_plan_mask(plan, si, cache)
+        ks, vs = kv[si]
+        _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, step_index, o=o, lse=lse,
+                                         stream=stream, events=events)
+        return info
+
+    for s in range(args.warmup):
+        run(s)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    K = args.steps
+    evs = [(dita.Event(), dita.Event(), dita.Event()) for _ in range(K)]
+    t_begin, t_end = dita.Event(), dita.Event()
+    infos = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        e = evs[i]
+        infos.append(run(args.warmup + i, events=(e[0].handle, e[1].handle, e[2].handle)))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_ms(t_end)
+    attn_ms = [e[0].elapsed_ms(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_ms(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_ms(e[2]) for e in evs]
+    fresh_flops = sum(i.fresh_flops for i in infos)
+    fresh_blocks = sum(i.n_fresh for i in infos)
+    merge_bytes = sum(i.merge_bytes for i in infos)
+    launches = sum(1 for i in infos if i.n_fresh > 0)
+    attn_s = sum(a for a, i in zip(attn_ms, infos) if i.n_fresh > 0) / 1e3
+    achieved = fresh_flops / attn_s / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    merge_gbs = merge_bytes / (sum(merge_ms) / 1e3) / 1e9
+    log(f"[bench] timed {K} steps: {total_ms:.3f} ms (host wall {wall * 1e3:.1f} ms); "
+        f"attention {sum(attn_ms):.3f} ms, merge {sum(merge_ms):.3f} ms")
+
+    result = {
+        "metric": "fresh-block attention TFLOP/s + ms per rank-step, 75,600-token DiT attn",
+        "value": fresh_flops / (total_ms / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "tokens": wl.N,
+            "grid_thw": list(wl.grid), "partitions": wl.P, "tokens_per_partition": wl.Nk,
+            "query_partition": wl.q_part, "schedule_steps": n_sched,
+            "mask": {"policy": ["distance", "k-nearest", "random", "ramp"][wl.policy],
+                     "radius": wl.radius, "radius_end": wl.radius_end, "k_nearest": wl.k_nearest,
+                     "anchor_period": wl.anchor_period},
+            "parallelism": "one rank's share on one GPU",
+        },
+        "fresh_blocks": fresh_blocks,
+        "fresh_fraction": fresh_blocks / (K * wl.P),
+        "fresh_tflop": fresh_flops / 1e12,
+        "attn_ms_per_step": sum(attn_ms) / K,
+        "merge_ms_per_step": sum(merge_ms) / K,
+        "step_ms": [round(x, 4) for x in step_ms],
+        "roofline": {
+            "kernel": "attn_fwd_bf16_kernel (grouped fresh partial attention)"
+            if wl.dtype == "bf16" else "attn_fwd_f32_kernel",
+            "bound": "mfma" if wl.dtype == "bf16" else "alu",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "launches": launches,
+            "avg_launch_ms": attn_s * 1e3 / max(launches, 1),
+            "flops_per_launch": fresh_flops / max(launches, 1),
+        },
+        "merge": {
+            "kernel": "merge_kernel", "bound": "hbm",
+            "achieved": merge_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": merge_gbs / PEAK_HBM_GBS, "bytes_per_launch": merge_bytes / K,
+            "avg_launch_ms": sum(merge_ms) / K,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

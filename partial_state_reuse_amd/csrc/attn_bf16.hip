@@ -9,29 +9,34 @@
 // Mapping onto CDNA4
 // ------------------
 // * A workgroup owns BM = 128 queries of one (batch, head) and one fresh
-//   partition (grid.z selects the job of a grouped launch); each of its four
-//   waves owns 32 queries.
+//   partition of a grouped launch; each of its four waves owns 32 queries.
+//   Workgroup ids are remapped so that all query tiles of one (head,
+//   partition) run on the same XCD and share its L2 copy of K and V.
+// * K and V tiles (BN keys x D) travel HBM -> LDS with direct-to-LDS loads
+//   (global_load_lds_dwordx4): no staging registers.  Both stay row-major in
+//   LDS with the 16-byte chunks of each row XOR-swizzled (chunk c of row r at
+//   c ^ swz(r)) so that the K reads and the transposed V reads below are free
+//   of bank conflicts.  Two stages; one barrier per tile.
 // * Scores are produced transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of the
-//   K tile (LDS), the B operand the wave's Q^T slice, held in registers for
-//   the whole kernel.  In the 32x32 accumulator every lane then owns ONE query
-//   (column) and 16 of the 32 keys; its partner lane (lane ^ 32) owns the
-//   other 16.  Row max and row sum need no more than one cross-lane exchange.
+//   K tile, the B operand the wave's Q^T slice, held in registers for the
+//   whole kernel.  In the 32x32 accumulator every lane owns ONE query and 16
+//   of the 32 keys; its partner lane (lane ^ 32) owns the other 16.
 // * The probabilities feed O^T += V^T P^T directly from registers: for the
-//   B operand a lane must supply 8 keys of its own query, and the 8
-//   accumulator entries of one half of the S^T block are exactly that (keys
-//   {0-3, 8-11} in the low half-wave, {4-7, 12-15} in the high one).  V^T is
-//   laid out in LDS with the same key permutation inside every group of 16
-//   keys, so the A operand is one 16-byte LDS read per lane.
+//   B operand a lane supplies 8 keys of its own query, and the 8 accumulator
+//   entries of one half of an S^T block are exactly that (keys {0-3, 8-11}
+//   in the low half-wave, {4-7, 12-15} in the high one).  The matching A
+//   operand (8 keys x one head-dim column of V) comes from two LDS transpose
+//   reads (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element
+//   i%4 of the rows addressed by lanes i/4 + {0,4,8,12}, so pointing lane x
+//   at key (x/4) and head-dim offset 4*(x%4) hands every lane 4 keys of its
+//   own column.
 // * The output accumulator O^T again gives each lane one query, so the
-//   online-softmax rescale and the final 1/l are per-lane scalars.
-// * Rescaling is lazy: the running max only moves (and O, l are rescaled) when
-//   a tile's max exceeds it by more than 2^8 in the exp2 domain; otherwise the
-//   stale max is kept, which is exact because numerator and denominator use
-//   the same reference.
-// * K and V tiles are fetched into registers one tile ahead (coalesced
-//   16-byte loads) and written to double-buffered LDS: K row-major with a
-//   16-byte row pad, V transposed with a 16-byte row pad.  One barrier per tile.
+//   online-softmax rescale and the final 1/l are per-lane scalars.  Rescaling
+//   is lazy: the running max only moves (and O, l are rescaled) when a
+//   tile's max exceeds it by more than 2^8 in the exp2 domain.
+// * The denominator sums the fp32 probabilities (LSE keeps fp32 accuracy);
+//   the P V product uses them rounded to bf16.
 // * Ragged tails: query rows past Nq load a clamped row and are not stored;
 //   key rows past nk load a clamped row and their scores are set to -inf.
 
@@ -44,33 +49,43 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the running max
+constexpr int kXcds = 8;
 
 template <int D>
 struct Tile {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int BM = kWaves * 32;           // queries per workgroup
-  static constexpr int BN = 8192 / D;              // keys per tile: 64 (D=128), 128 (D=64)
-  static constexpr int KS = D + 8;                 // K row stride in LDS (elements)
-  static constexpr int VS = BN + 8;                // V^T row stride in LDS (elements)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = BN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int V_GROUPS = BN / 4;                 // 4-key groups per tile
-  static_assert(V_GROUPS * (D / 8) == kThreads, "one 4x8 V block per thread");
-  static_assert(K_CHUNKS * kThreads * 8 == BN * D, "K tile split");
+  static constexpr int BM = kWaves * 32;             // queries per workgroup
+  static constexpr int BN = 8192 / D;                // keys per tile: 64 (D=128), 128 (D=64)
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K then V
+  static constexpr int NSTAGE = 2;
+  static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tensor
+  static_assert(LOADS * kThreads == BN * CPR, "tile split");
 };
 
-__device__ inline u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Chunk swizzle of row r.  D=128 (16 chunks per row): the 16 rows read together
+// by K fragments hit 16 distinct chunk slots, and the 4 consecutive rows x 4
+// chunks read together by V transpose fragments hit 16 distinct slots.  D=64 (8
+// chunks, two rows per 64 banks): the same two properties with row parity.
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
+__device__ inline u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ inline f32x16 zero16() {
@@ -80,26 +95,37 @@ __device__ inline f32x16 zero16() {
   return z;
 }
 
-// Position, inside the V^T row of a tile, of key 4*g (the 4-key group g).
-// Inside every 16-key group, key 8a + 4h + r lives at 8h + 4a + r.
-__device__ inline int vt_pos(int g) { return 16 * (g >> 2) + 8 * (g & 1) + 4 * ((g >> 1) & 1); }
+// Bijection of [0, n) that gives each XCD (workgroups are dispatched to XCDs
+// round-robin) one contiguous range of logical tiles.
+__device__ inline int64_t xcd_remap(int64_t pid, int64_t n) {
+  const int64_t per = (n + kXcds - 1) / kXcds;
+  const int64_t tall = n % kXcds == 0 ? kXcds : n % kXcds;
+  const int64_t xcd = pid % kXcds, local = pid / kXcds;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __restrict__ q,
-                                                            AttnJobs jobs, int64_t Nq,
-                                                            float scale_log2) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __restrict__ q,
+                                                               AttnJobs jobs, int64_t Nq, int BH,
+                                                               int QT, float scale_log2) {
   using T = Tile<D>;
   constexpr int NB = T::BN / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;      // MFMA k-steps over the head dim
   constexpr int ND = D / 32;       // 32-wide blocks of the head dim
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::BUF_ELEMS];
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE_BYTES];
 
-  const AttnJob& job = jobs.job[blockIdx.z];
-  const int64_t bh = blockIdx.y;
+  const int64_t n_tiles = int64_t(gridDim.x);
+  const int64_t lin = xcd_remap(blockIdx.x, n_tiles);
+  const int qt = int(lin % QT);
+  const int64_t rest = lin / QT;
+  const int64_t bh = rest % BH;
+  const int jid = int(rest / BH);
+
+  const AttnJob& job = jobs.job[jid];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t nk = job.nk;
@@ -109,7 +135,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __rest
   const __bf16* __restrict__ qp = q + bh * Nq * D;
 
   // Q^T operand: lane holds Q[row][kk*16 + 8*hh .. +7] for every k-step kk.
-  const int64_t qrow = int64_t(blockIdx.x) * T::BM + wave * 32 + m32;
+  const int64_t qrow = int64_t(qt) * T::BM + wave * 32 + m32;
   const int64_t qrow_c = qrow < Nq ? qrow : Nq - 1;
   bf16x8 qf[NKK];
 #pragma unroll
@@ -119,74 +145,56 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __rest
 #pragma unroll
   for (int d = 0; d < ND; ++d) oacc[d] = zero16();
   float m_run = -INFINITY;  // running max, exp2 domain
-  float l_run = 0.0f;       // this lane's partial denominator (its 16 keys per block)
+  float l_run = 0.0f;       // this lane's partial denominator
 
   const int ntiles = int((nk + T::BN - 1) / T::BN);
 
-  // Per-thread global->register staging of one tile.
-  u32x4 kreg[T::K_CHUNKS];
-  u32x4 vreg[4];
-  const int vg = tid % T::V_GROUPS;  // 4-key group
-  const int vc = tid / T::V_GROUPS;  // 8-wide head-dim chunk
-
-  auto fetch = [&](int t) {
+  // Direct-to-LDS fetch of tile t into stage st: LDS slot s (16 bytes) holds
+  // chunk (s % CPR) ^ swz(row) of row s / CPR.  The LDS destination of a wave's
+  // load is lane-linear; the global source is chosen to match.
+  auto fetch = [&](int t, int st) {
     const int64_t kbase = int64_t(t) * T::BN;
+    char* kst = smem + st * T::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < T::K_CHUNKS; ++i) {
-      const int id = tid + i * T::kThreads;
-      const int row = id / (D / 8);
-      const int col = id % (D / 8);
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int s = tid + i * T::kThreads;
+      const int row = s / T::CPR;
+      const int c = (s % T::CPR) ^ swz<D>(row);
       int64_t r = kbase + row;
       r = r < nk ? r : nk - 1;
-      kreg[i] = load16(kp + r * D + col * 8);
-    }
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      int64_t r = kbase + 4 * vg + r4;
-      r = r < nk ? r : nk - 1;
-      vreg[r4] = load16(vp + r * D + vc * 8);
+      const int64_t goff = r * D + c * 8;
+      char* dst = kst + (wave * 64 + i * T::kThreads) * 16;
+      __builtin_amdgcn_global_load_lds(kp + goff, (lds_void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + goff, (lds_void*)(dst + T::TILE_BYTES), 16, 0, 0);
     }
   };
 
-  auto stash = [&](__bf16* ks, __bf16* vs) {
-#pragma unroll
-    for (int i = 0; i < T::K_CHUNKS; ++i) {
-      const int id = tid + i * T::kThreads;
-      const int row = id / (D / 8);
-      const int col = id % (D / 8);
-      *reinterpret_cast<u32x4*>(ks + row * T::KS + col * 8) = kreg[i];
-    }
-    const int pos = vt_pos(vg);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // head-dim 8*vc + 2w (low halves) and 8*vc + 2w + 1 (high halves) of the 4 keys
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(vs + (8 * vc + 2 * w) * T::VS + pos) = lo;
-      *reinterpret_cast<u32x2*>(vs + (8 * vc + 2 * w + 1) * T::VS + pos) = hi;
-    }
-  };
+  // Per-lane pieces of the V transpose-read addresses (see the header comment).
+  const int g16 = lane & 15;
+  const int gh = (lane >> 4) & 1;
+  const int v_row0 = 4 * hh + (g16 >> 2);      // + 32*b + 16*ks2 + 8*r2
+  const int v_cpart = 2 * gh + ((g16 & 3) >> 1);  // chunk = 4*db + v_cpart
+  const int v_byte = 8 * (g16 & 1);
 
-  fetch(0);
+  fetch(0, 0);
   for (int t = 0; t < ntiles; ++t) {
-    __bf16* ks = smem + (t & 1) * T::BUF_ELEMS;
-    __bf16* vs = ks + T::K_ELEMS;
-    stash(ks, vs);
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of tile t have landed
+    __syncthreads();                 // ... everyone's; and everyone is done with tile t-1
+    if (t + 1 < ntiles) fetch(t + 1, (t + 1) & 1);
+    const char* kst = smem + (t & 1) * T::STAGE_BYTES;
+    const char* vst = kst + T::TILE_BYTES;
 
     // S^T = K Q^T for the tile: NB blocks of 32 keys x 32 queries.
     f32x16 s[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       s[b] = zero16();
+      const int row = b * 32 + m32;
+      const char* krow = kst + row * T::ROW_BYTES;
+      const int sw = swz<D>(row);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(ks + (b * 32 + m32) * T::KS + kk * 16 + 8 * hh));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ((2 * kk + hh) ^ sw)));
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[b], 0, 0, 0);
       }
     }
@@ -222,8 +230,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __rest
       m_run = m_new;
     }
 
-    // P = exp2(S * scale*log2e - m): fp32 for the denominator (so LSE keeps fp32
-    // accuracy), rounded to bf16 for the P V product.
+    // P = exp2(S * scale*log2e - m): fp32 for the denominator, bf16 for P V.
     bf16x8 pb[NB][2];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -241,15 +248,23 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __rest
         pb[b][h2] = v;
       }
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T; the V^T operand comes from two transpose reads per MFMA.
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              vs + (d * 32 + m32) * T::VS + b * 32 + h2 * 16 + 8 * hh));
+          s16x4 part[2];
+#pragma unroll
+          for (int r2 = 0; r2 < 2; ++r2) {
+            const int row = 32 * b + 16 * h2 + 8 * r2 + v_row0;
+            const int c = (4 * d + v_cpart) ^ swz<D>(row);
+            part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(vst + row * T::ROW_BYTES + 16 * c + v_byte));
+          }
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][h2], oacc[d], 0, 0, 0);
         }
   }
@@ -270,23 +285,23 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(const __bf16* __rest
   if (hh == 0) job.lse[bh * Nq + qrow] = (m_run + __builtin_log2f(l_tot)) * kLn2;
 }
 
+template <int D>
+hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
+                    hipStream_t stream) {
+  using T = Tile<D>;
+  const int QT = int((pr.Nq + T::BM - 1) / T::BM);
+  const int64_t n = int64_t(QT) * pr.BH * n_jobs;
+  attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), T::kThreads, 0, stream>>>(
+      static_cast<const __bf16*>(q), jobs, pr.Nq, pr.BH, QT, pr.scale * kLog2e);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                             hipStream_t stream) {
-  const float sl2 = pr.scale * kLog2e;
-  if (pr.D == 128) {
-    using T = Tile<128>;
-    dim3 grid(unsigned((pr.Nq + T::BM - 1) / T::BM), unsigned(pr.BH), unsigned(n_jobs));
-    attn_fwd_bf16_kernel<128><<<grid, T::kThreads, 0, stream>>>(static_cast<const __bf16*>(q), jobs,
-                                                                pr.Nq, sl2);
-  } else {
-    using T = Tile<64>;
-    dim3 grid(unsigned((pr.Nq + T::BM - 1) / T::BM), unsigned(pr.BH), unsigned(n_jobs));
-    attn_fwd_bf16_kernel<64><<<grid, T::kThreads, 0, stream>>>(static_cast<const __bf16*>(q), jobs,
-                                                               pr.Nq, sl2);
-  }
-  return hipGetLastError();
+  return pr.D == 128 ? launch_d<128>(pr, q, jobs, n_jobs, stream)
+                     : launch_d<64>(pr, q, jobs, n_jobs, stream);
 }
 
 }  // namespace dita
