@@ -53,7 +53,31 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--resident-steps", type=int, default=0,
+                    help="distinct K/V steps to generate (0: the whole schedule); step s uses "
+                         "inputs s mod this, for short profiling runs")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run the library's state-copy kernel over BYTES of O (the "
+                         "reference point for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    """Copy a state of known size with the library's copy kernel (cache store), 5 times."""
+    import torch
+    import partial_state_reuse_amd as dita
+    dev = torch.device("cuda:0")
+    D, H = 128, 1
+    nq = max(1, nbytes // (D * 2))
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P=1, device=dev)
+    o = torch.zeros((1, H, nq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((1, H, nq), dtype=torch.float32, device=dev)
+    for i in range(5):
+        cache.store(0, o, lse, step=i)
+    torch.cuda.synchronize()
+    moved = nq * D * 2 + nq * 4
+    print(json.dumps({"copy_calibration": {"launches": 5, "read_bytes_per_launch": moved,
+                                           "write_bytes_per_launch": moved}}), flush=True)
 
 
 def upload_parts(x: np.ndarray, wl, dev, tdt):
@@ -117,6 +141,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "design is described in DESIGN.md and not built.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import partial_state_reuse_amd as dita
     import workloads
@@ -126,13 +153,14 @@ def main():
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     n_sched = wl.steps
+    n_res = n_sched if args.resident_steps <= 0 else min(args.resident_steps, n_sched)
     log(f"[bench] {wl.name}: B={wl.B} H={wl.H} D={wl.D} N={wl.N} P={wl.P} Nk={wl.Nk} "
-        f"dtype={wl.dtype}; generating {n_sched} steps of inputs")
+        f"dtype={wl.dtype}; generating {n_res} steps of inputs")
     t_gen = time.perf_counter()
     inp = Inputs(wl, seed=args.seed)
     q = torch.from_numpy(inp.q).to(tdt).to(dev)
     kv = []
-    for s in range(n_sched):
+    for s in range(n_res):
         k, v = inp.kv(s)
         kv.append((upload_parts(k, wl, dev, tdt), upload_parts(v, wl, dev, tdt)))
         log(f"[bench] inputs for schedule step {s} resident")
@@ -148,7 +176,7 @@ def main():
     def run(step_index, events=None):
         si = step_index % n_sched
         mask = dita.dita_plan_mask(plan, si, cache)
-        ks, vs = kv[si]
+        ks, vs = kv[si % n_res]
         _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, step_index, o=o, lse=lse,
                                          stream=stream, events=events)
         return info
@@ -202,7 +230,7 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "tokens": wl.N,
             "grid_thw": list(wl.grid), "partitions": wl.P, "tokens_per_partition": wl.Nk,
-            "query_partition": wl.q_part, "schedule_steps": n_sched,
+            "query_partition": wl.q_part, "schedule_steps": n_sched, "resident_input_steps": n_res,
             "mask": {"policy": ["distance", "k-nearest", "random", "ramp"][wl.policy],
                      "radius": wl.radius, "radius_end": wl.radius_end, "k_nearest": wl.k_nearest,
                      "anchor_period": wl.anchor_period},

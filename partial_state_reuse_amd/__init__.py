@@ -68,7 +68,7 @@ def _load() -> ctypes.CDLL:
     # load a second HIP runtime into the process.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m partial_state_reuse_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python partial_state_reuse_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t

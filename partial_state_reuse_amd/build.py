@@ -1,7 +1,10 @@
 """Build libdita.so (HIP for gfx950 + host C++) in-tree with hipcc.
 
-Usage: ``python -m partial_state_reuse_amd.build`` or ``build()`` from Python.
-Every call recompiles every source.
+Usage: ``python partial_state_reuse_amd/build.py [-v]`` (run as a script, so that
+importing the package -- which loads the library -- is never needed to build
+it), or ``build()`` after loading this file by path.  Every call recompiles
+every source, then checks that the linked library leaves no symbol of its own
+undefined.
 """
 
 from __future__ import annotations
@@ -64,8 +67,20 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     if rc:
         sys.stderr.write(out + "\n")
         raise RuntimeError("link failed")
+    _check_symbols(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_symbols(lib: str) -> None:
+    """Fail on undefined symbols of the library's own (e.g. a kernel launch stub the
+    host pass did not emit): dlopen would reject such a library at run time."""
+    r = subprocess.run(["nm", "-u", "-C", lib], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True)
+    bad = [ln.strip() for ln in r.stdout.splitlines()
+           if "dita" in ln or "__device_stub" in ln]
+    if r.returncode or bad:
+        raise RuntimeError("libdita.so has undefined symbols of its own:\n" + "\n".join(bad))
 
 
 if __name__ == "__main__":

@@ -12,11 +12,18 @@
 //   partition of a grouped launch; each of its four waves owns 32 queries.
 //   Workgroup ids are remapped so that all query tiles of one (head,
 //   partition) run on the same XCD and share its L2 copy of K and V.
-// * K and V tiles (BN keys x D) travel HBM -> LDS with direct-to-LDS loads
-//   (global_load_lds_dwordx4): no staging registers.  Both stay row-major in
-//   LDS with the 16-byte chunks of each row XOR-swizzled (chunk c of row r at
-//   c ^ swz(r)) so that the K reads and the transposed V reads below are free
-//   of bank conflicts.  Two stages; one barrier per tile.
+// * K and V tiles (BN keys x D) travel HBM -> LDS with direct-to-LDS buffer
+//   loads (buffer_load_dwordx4 ... lds): no staging registers, a per-lane
+//   offset fixed for the whole kernel plus a scalar per-tile offset, and rows
+//   past the partition end read as zero.  Both stay row-major in LDS with the
+//   16-byte chunks of each row XOR-swizzled (chunk c of row r at c ^ swz(r))
+//   so that the K reads and the transposed V reads below are free of bank
+//   conflicts.  K runs one tile ahead of V (two stages each); one barrier per
+//   tile.
+// * Software pipeline inside every wave: the exponentials of tile t are
+//   issued beside the S MFMAs of tile t+1, and the row max of tile t+1 beside
+//   the P V MFMAs of tile t, so the VALU and the matrix cores overlap even
+//   within a single wave.
 // * Scores are produced transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of the
 //   K tile, the B operand the wave's Q^T slice, held in registers for the
@@ -38,7 +45,7 @@
 // * The denominator sums the fp32 probabilities (LSE keeps fp32 accuracy);
 //   the P V product uses them rounded to bf16.
 // * Ragged tails: query rows past Nq load a clamped row and are not stored;
-//   key rows past nk load a clamped row and their scores are set to -inf.
+//   key rows past nk load as zero and their scores are set to -inf.
 
 #include "dita_kernels.h"
 
@@ -60,31 +67,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the running max
 constexpr int kXcds = 8;
 
-template <int D>
-struct Tile {
-  static constexpr int kWaves = 4;
-  static constexpr int kThreads = kWaves * 64;
-  static constexpr int BM = kWaves * 32;             // queries per workgroup
-  static constexpr int BN = 8192 / D;                // keys per tile: 64 (D=128), 128 (D=64)
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // 16 KiB
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K then V
-  static constexpr int NSTAGE = 2;
-  static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tensor
-  static_assert(LOADS * kThreads == BN * CPR, "tile split");
-};
-
-// Chunk swizzle of row r.  D=128 (16 chunks per row): the 16 rows read together
-// by K fragments hit 16 distinct chunk slots, and the 4 consecutive rows x 4
-// chunks read together by V transpose fragments hit 16 distinct slots.  D=64 (8
-// chunks, two rows per 64 banks): the same two properties with row parity.
-template <int D>
-__device__ inline int swz(int r) {
-  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
 __device__ inline u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -105,18 +87,88 @@ __device__ inline int64_t xcd_remap(int64_t pid, int64_t n) {
 }
 
 template <int D>
+struct Tile {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int BM = kWaves * 32;             // queries per workgroup
+  static constexpr int BN = 4096 / D;                // keys per tile: 32 (D=128), 64 (D=64)
+  static constexpr int ROW_BYTES = D * 2;            // one K or V row in HBM
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int KS = ROW_BYTES + 16;          // K row stride in LDS
+  static constexpr int VS = ROW_BYTES + 64;          // V row stride in LDS
+  static constexpr int K_SPR = KS / 16;              // 16-byte LDS slots per K row
+  static constexpr int V_SPR = VS / 16;
+  static constexpr int K_REGION = (BN * KS + 1023) / 1024 * 1024;  // whole wave loads
+  static constexpr int V_REGION = (BN * VS + 1023) / 1024 * 1024;
+  static constexpr int K_WLOADS = K_REGION / 1024;   // wave-wide 16-byte loads per K tile
+  static constexpr int V_WLOADS = V_REGION / 1024;
+  static constexpr int K_PER_WAVE = (K_WLOADS + kWaves - 1) / kWaves;
+  static constexpr int V_PER_WAVE = (V_WLOADS + kWaves - 1) / kWaves;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // bytes of one tile in HBM
+  static constexpr int LDS_BYTES = 2 * K_REGION + 2 * V_REGION;
+};
+
+// Byte offset, inside a tile in HBM, that fills LDS slot `slot` of a region
+// whose rows are `spr` slots long; padding slots get an offset past any
+// buffer's end, which the buffer load turns into zeros without a memory access.
+__device__ inline uint32_t slot_offset(int slot, int spr, int rows, int cpr, int row_bytes) {
+  const int row = slot / spr, col = slot % spr;
+  return (row < rows && col < cpr) ? uint32_t(row * row_bytes + col * 16) : 0x7ffffff0u;
+}
+
+// One tile HBM -> LDS: wave w issues wave-loads w, w + 4, ...; wave-load i fills
+// LDS slots [64 i, 64 i + 64) of `region` (lane-linear), lane data from off[j].
+// (A plain device function: the buffer-resource builtins inside a lambda make
+// the host pass drop the kernel's launch stub.)
+template <int PER_WAVE, int WLOADS>
+__device__ inline void load_region(__amdgpu_buffer_rsrc_t r, char* region, int wave,
+                                   const uint32_t* off) {
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int i = wave + 4 * j;
+    if (i < WLOADS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(region + i * 1024), 16, off[j], 0, 0, 0);
+  }
+}
+
+// Buffer resource over tile t of one head's K or V: records end at the
+// partition end, so rows past nk read as zero.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* head, int t, int tile_bytes,
+                                                   uint32_t head_bytes) {
+  const uint32_t start = uint32_t(t) * uint32_t(tile_bytes);
+  const uint32_t left = head_bytes > start ? head_bytes - start : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head + start), 0, int(left), 0x00020000);
+}
+
+template <int D>
+__device__ inline void load_k_tile(const char* head, int t, uint32_t head_bytes, char* region,
+                                   int wave, const uint32_t* off) {
+  using T = Tile<D>;
+  load_region<T::K_PER_WAVE, T::K_WLOADS>(tile_rsrc(head, t, T::TILE_BYTES, head_bytes), region,
+                                          wave, off);
+}
+
+template <int D>
+__device__ inline void load_v_tile(const char* head, int t, uint32_t head_bytes, char* region,
+                                   int wave, const uint32_t* off) {
+  using T = Tile<D>;
+  load_region<T::V_PER_WAVE, T::V_WLOADS>(tile_rsrc(head, t, T::TILE_BYTES, head_bytes), region,
+                                          wave, off);
+}
+
+template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __restrict__ q,
-                                                               AttnJobs jobs, int64_t Nq, int BH,
+                                                               AttnJobs jobs, int Nq, int BH,
                                                                int QT, float scale_log2) {
   using T = Tile<D>;
   constexpr int NB = T::BN / 32;   // 32-key blocks per tile
   constexpr int NKK = D / 16;      // MFMA k-steps over the head dim
   constexpr int ND = D / 32;       // 32-wide blocks of the head dim
 
-  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE_BYTES];
+  // K stage 0, K stage 1, V stage 0, V stage 1.  K runs one tile ahead of V.
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
-  const int64_t n_tiles = int64_t(gridDim.x);
-  const int64_t lin = xcd_remap(blockIdx.x, n_tiles);
+  const int64_t lin = xcd_remap(blockIdx.x, int64_t(gridDim.x));
   const int qt = int(lin % QT);
   const int64_t rest = lin / QT;
   const int64_t bh = rest % BH;
@@ -128,18 +180,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __r
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m32 = lane & 31;
   const int hh = lane >> 5;
-  const int64_t nk = job.nk;
+  const int nk = int(job.nk);
+  const int ntiles = (nk + T::BN - 1) / T::BN;
 
-  const __bf16* __restrict__ kp = static_cast<const __bf16*>(job.k) + bh * nk * D;
-  const __bf16* __restrict__ vp = static_cast<const __bf16*>(job.v) + bh * nk * D;
-  const __bf16* __restrict__ qp = q + bh * Nq * D;
+  const uint32_t head_bytes = uint32_t(nk) * T::ROW_BYTES;
+  const char* k_head = reinterpret_cast<const char*>(job.k) + bh * int64_t(head_bytes);
+  const char* v_head = reinterpret_cast<const char*>(job.v) + bh * int64_t(head_bytes);
+  uint32_t k_off[T::K_PER_WAVE], v_off[T::V_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < T::K_PER_WAVE; ++j)
+    k_off[j] = slot_offset((wave + 4 * j) * 64 + lane, T::K_SPR, T::BN, T::CPR, T::ROW_BYTES);
+#pragma unroll
+  for (int j = 0; j < T::V_PER_WAVE; ++j)
+    v_off[j] = slot_offset((wave + 4 * j) * 64 + lane, T::V_SPR, T::BN, T::CPR, T::ROW_BYTES);
+  char* const k_stage0 = smem;
+  char* const v_stage0 = smem + 2 * T::K_REGION;
+
+  load_k_tile<D>(k_head, 0, head_bytes, k_stage0, wave, k_off);
+  if (ntiles > 1) load_k_tile<D>(k_head, 1, head_bytes, k_stage0 + T::K_REGION, wave, k_off);
+  load_v_tile<D>(v_head, 0, head_bytes, v_stage0, wave, v_off);
 
   // Q^T operand: lane holds Q[row][kk*16 + 8*hh .. +7] for every k-step kk.
-  const int64_t qrow = int64_t(qt) * T::BM + wave * 32 + m32;
-  const int64_t qrow_c = qrow < Nq ? qrow : Nq - 1;
+  const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
+  const int qrow = qt * T::BM + wave * 32 + m32;
+  const int qrow_c = qrow < Nq ? qrow : Nq - 1;
   bf16x8 qf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(load16(qp + qrow_c * D + kk * 16 + 8 * hh));
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = as_bf16x8(load16(qp + int64_t(qrow_c) * D + kk * 16 + 8 * hh));
+
+  // Per-lane LDS read offsets; everything else is a compile-time immediate.
+  //   K fragment (block b, k-step kk): row 32b + m32, bytes [32kk + 16hh, +16).
+  //   V transpose read (block b, half h2, read r2, head-dim block d): lane x of a
+  //   16-lane group addresses row 32b + 16h2 + 8r2 + 4hh + x/4, head-dim
+  //   32d + 16gh + 4(x%4), four elements.
+  const int k_lane = m32 * T::KS + 16 * hh;
+  const int g16 = lane & 15;
+  const int gh = (lane >> 4) & 1;
+  const int v_lane = (4 * hh + (g16 >> 2)) * T::VS + 32 * gh + 8 * (g16 & 3);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -147,91 +225,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __r
   float m_run = -INFINITY;  // running max, exp2 domain
   float l_run = 0.0f;       // this lane's partial denominator
 
-  const int ntiles = int((nk + T::BN - 1) / T::BN);
-
-  // Direct-to-LDS fetch of tile t into stage st: LDS slot s (16 bytes) holds
-  // chunk (s % CPR) ^ swz(row) of row s / CPR.  The LDS destination of a wave's
-  // load is lane-linear; the global source is chosen to match.
-  auto fetch = [&](int t, int st) {
-    const int64_t kbase = int64_t(t) * T::BN;
-    char* kst = smem + st * T::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int s = tid + i * T::kThreads;
-      const int row = s / T::CPR;
-      const int c = (s % T::CPR) ^ swz<D>(row);
-      int64_t r = kbase + row;
-      r = r < nk ? r : nk - 1;
-      const int64_t goff = r * D + c * 8;
-      char* dst = kst + (wave * 64 + i * T::kThreads) * 16;
-      __builtin_amdgcn_global_load_lds(kp + goff, (lds_void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + goff, (lds_void*)(dst + T::TILE_BYTES), 16, 0, 0);
-    }
-  };
-
-  // Per-lane pieces of the V transpose-read addresses (see the header comment).
-  const int g16 = lane & 15;
-  const int gh = (lane >> 4) & 1;
-  const int v_row0 = 4 * hh + (g16 >> 2);      // + 32*b + 16*ks2 + 8*r2
-  const int v_cpart = 2 * gh + ((g16 & 3) >> 1);  // chunk = 4*db + v_cpart
-  const int v_byte = 8 * (g16 & 1);
-
-  fetch(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of tile t have landed
-    __syncthreads();                 // ... everyone's; and everyone is done with tile t-1
-    if (t + 1 < ntiles) fetch(t + 1, (t + 1) & 1);
-    const char* kst = smem + (t & 1) * T::STAGE_BYTES;
-    const char* vst = kst + T::TILE_BYTES;
-
-    // S^T = K Q^T for the tile: NB blocks of 32 keys x 32 queries.
-    f32x16 s[NB];
+  auto compute_s = [&](const char* kreg, f32x16* s) {
+    const char* kb0 = kreg + k_lane;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       s[b] = zero16();
-      const int row = b * 32 + m32;
-      const char* krow = kst + row * T::ROW_BYTES;
-      const int sw = swz<D>(row);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 16 * ((2 * kk + hh) ^ sw)));
+        const bf16x8 a =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(kb0 + b * 32 * T::KS + 32 * kk));
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[b], 0, 0, 0);
       }
     }
-
-    // Keys past the partition end score -inf.
-    if (int64_t(t + 1) * T::BN > nk) {
-      const int64_t kb0 = int64_t(t) * T::BN;
+  };
+  // Keys past the partition end score -inf (only the last tile has any).
+  auto mask_tail = [&](int t, f32x16* s) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = kb0 + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= nk) s[b][i] = -INFINITY;
-        }
-    }
-
-    // Row max of raw scores (scale > 0 commutes with max), then the pair exchange.
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * T::BN + b * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= nk) s[b][i] = -INFINITY;
+      }
+  };
+  auto row_max = [&](const f32x16* s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * scale_log2;
-    const float m_new = fmaxf(m_run, m_tile);
-    if (__any(m_new > m_run + kRescaleSlack)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-      m_run = m_new;
-    }
-
-    // P = exp2(S * scale*log2e - m): fp32 for the denominator, bf16 for P V.
-    bf16x8 pb[NB][2];
+    return mx;
+  };
+  // P = exp2(S * scale*log2e - m): fp32 into the denominator, bf16 for P V.
+  auto softmax = [&](const f32x16* s, bf16x8 (*pb)[2]) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -247,8 +273,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __r
         l_run += part;
         pb[b][h2] = v;
       }
-
-    // O^T += V^T P^T; the V^T operand comes from two transpose reads per MFMA.
+  };
+  // O^T += V^T P^T; the V^T operand comes from two transpose reads per MFMA.
+  auto pv = [&](const char* vreg, bf16x8 (*pb)[2]) {
+    const char* vb0 = vreg + v_lane;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -257,22 +285,84 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const __bf16* __r
         for (int h2 = 0; h2 < 2; ++h2) {
           s16x4 part[2];
 #pragma unroll
-          for (int r2 = 0; r2 < 2; ++r2) {
-            const int row = 32 * b + 16 * h2 + 8 * r2 + v_row0;
-            const int c = (4 * d + v_cpart) ^ swz<D>(row);
+          for (int r2 = 0; r2 < 2; ++r2)
             part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(vst + row * T::ROW_BYTES + 16 * c + v_byte));
-          }
+                (lds_s16x4*)(vb0 + (32 * b + 16 * h2 + 8 * r2) * T::VS + 64 * d));
           const bf16x8 a = __builtin_bit_cast(
               bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][h2], oacc[d], 0, 0, 0);
         }
+  };
+  auto rescale = [&](float mx) {
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    if (__any(m_new > m_run + kRescaleSlack)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // Start of tile t: wait for K_{t+1} and V_t, free the stages of K_t and
+  // V_{t-1}, prefetch K_{t+2} and V_{t+1}, apply the tail mask, update the max.
+  auto head = [&](int t, f32x16* sc, float& mx) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's K_{t+1} and V_t have landed
+    __syncthreads();                // ... everyone's; K_t and V_{t-1} are no longer read
+    if (t + 2 < ntiles)
+      load_k_tile<D>(k_head, t + 2, head_bytes, k_stage0 + (t & 1) * T::K_REGION, wave, k_off);
+    if (t + 1 < ntiles)
+      load_v_tile<D>(v_head, t + 1, head_bytes, v_stage0 + ((t + 1) & 1) * T::V_REGION, wave,
+                     v_off);
+    if ((t + 1) * T::BN > nk) {
+      mask_tail(t, sc);
+      mx = row_max(sc);
+    }
+    rescale(mx);
+  };
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sc[NB];
+  compute_s(k_stage0, sc);
+  float mx = row_max(sc);
+
+  // Tiles with a successor: the exponentials of tile t are interleaved with the
+  // S MFMAs of tile t+1, and the P V MFMAs of tile t with the row max of tile
+  // t+1 (one basic block after the two rare branches in head()).
+  int t = 0;
+  for (; t + 1 < ntiles; ++t) {
+    head(t, sc, mx);
+    bf16x8 pb[NB][2];
+    f32x16 sn[NB];
+    softmax(sc, pb);
+    compute_s(k_stage0 + ((t + 1) & 1) * T::K_REGION, sn);
+    // About 3.5 VALU per score (fma, exp, add, half a convert): 56 per 32-key block.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NB * NKK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, (56 * NB + NB * NKK - 1) / (NB * NKK), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    pv(v_stage0 + (t & 1) * T::V_REGION, pb);
+    mx = row_max(sn);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sc[b] = sn[b];
+  }
+  {
+    head(t, sc, mx);
+    bf16x8 pb[NB][2];
+    softmax(sc, pb);
+    pv(v_stage0 + (t & 1) * T::V_REGION, pb);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow >= Nq) return;
   const float inv = 1.0f / l_tot;
-  __bf16* __restrict__ op = static_cast<__bf16*>(job.o) + bh * Nq * D + qrow * D;
+  __bf16* __restrict__ op = static_cast<__bf16*>(job.o) + (bh * Nq + qrow) * int64_t(D);
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -292,7 +382,7 @@ hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, 
   const int QT = int((pr.Nq + T::BM - 1) / T::BM);
   const int64_t n = int64_t(QT) * pr.BH * n_jobs;
   attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), T::kThreads, 0, stream>>>(
-      static_cast<const __bf16*>(q), jobs, pr.Nq, pr.BH, QT, pr.scale * kLog2e);
+      static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, QT, pr.scale * kLog2e);
   return hipGetLastError();
 }
 
