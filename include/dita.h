@@ -29,7 +29,8 @@
  *    V_p are [B, H, Nk_p, D]; LSE arrays are float32 [B, H, Nq].  O and O_p
  *    have the input dtype; LSE is always float32 and uses the natural log.
  *  - Device pointers must be 16-byte aligned.  D is 64 or 128.  B*H <= 65535,
- *    1 <= Nq, Nk <= 2^30, 1 <= P <= DITA_MAX_PARTITIONS.
+ *    1 <= Nq, Nk <= 2^30, Nk * D * sizeof(dtype) < 2^31 (one head's K or V
+ *    slice), 1 <= P <= DITA_MAX_PARTITIONS.
  *  - O_p is normalised by its own partition's softmax denominator (each row
  *    is a convex combination of V_p's rows); the unnormalised output is
  *    exp(LSE_p) * O_p.

@@ -67,6 +67,12 @@ size_t state_o_bytes(const dita_shape& s) {
 }
 size_t state_lse_bytes(const dita_shape& s) { return size_t(s.B) * size_t(s.H) * size_t(s.Nq) * 4; }
 
+// A K or V head slice must stay below 2^31 bytes: the attention kernel
+// addresses it through a buffer resource with a 32-bit record count.
+bool nk_ok(const dita_shape& s, int64_t nk) {
+  return nk >= 1 && nk <= kMaxRows && nk * int64_t(s.D) * int64_t(elem_size(s.dtype)) < (int64_t(1) << 31);
+}
+
 dita::AttnProblem problem(const dita_shape& s) {
   dita::AttnProblem pr;
   pr.BH = s.B * s.H;
@@ -127,7 +133,7 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
   if (st) return st;
   for (const void* p : {q, k, v, static_cast<const void*>(o_p), static_cast<const void*>(lse_p)})
     if ((st = check_dev(p))) return st;
-  if (nk < 1 || nk > kMaxRows) return DITA_ERR_SHAPE;
+  if (!nk_ok(*shape, nk)) return DITA_ERR_SHAPE;
   dita::AttnJobs jobs;
   jobs.job[0] = dita::AttnJob{k, v, o_p, lse_p, nk};
   return hip_status(launch_attn(*shape, q, jobs, 1, static_cast<hipStream_t>(stream)));
@@ -292,7 +298,7 @@ int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_
       continue;
     }
     if ((st = check_dev(k_list[p])) || (st = check_dev(v_list[p]))) return st;
-    if (nk_list[p] < 1 || nk_list[p] > kMaxRows) return DITA_ERR_SHAPE;
+    if (!nk_ok(s, nk_list[p])) return DITA_ERR_SHAPE;
     jobs.job[n_fresh++] = dita::AttnJob{k_list[p], v_list[p], slot_o(cache, p), slot_lse(cache, p),
                                         nk_list[p]};
     fresh_keys += double(nk_list[p]);

@@ -166,6 +166,10 @@ def test_attn_partial_rejects_bad_pointers_and_nk():
     assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 64, p, p + 4, None) == dita.DITA_ERR_ALIGN
     assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 0, p, p, None) == dita.DITA_ERR_SHAPE
     assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 2**31, p, p, None) == dita.DITA_ERR_SHAPE
+    # one head's K slice must stay below 2^31 bytes: 2^23 keys x 128 x 2 bytes is 2^31
+    assert lib.dita_attn_partial(ctypes.byref(shape), p, p, p, 2**23, p, p, None) == dita.DITA_ERR_SHAPE
+    f32 = dita.Shape(1, 2, 128, dita.DITA_F32, 64, 0.0)
+    assert lib.dita_attn_partial(ctypes.byref(f32), p, p, p, 2**22, p, p, None) == dita.DITA_ERR_SHAPE
 
 
 def test_state_merge_rejects_bad_arguments():
