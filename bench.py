@@ -135,6 +135,55 @@ def cpu_baseline(inp, wl, budget_s: float):
     }
 
 
+def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: int = 3):
+    """Merge and state-copy bandwidth outside the step, rotating over n_caches
+    caches (each bigger than the 256 MB last-level cache together) so that the
+    bytes come from HBM.  Each cache holds P valid slots of arbitrary data."""
+    import torch
+    caches = [dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev) for _ in range(n_caches)]
+    o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
+    lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+    src_o = torch.randn((wl.B, wl.H, wl.Nq, wl.D), device=dev).to(tdt)
+    src_l = torch.randn((wl.B, wl.H, wl.Nq), device=dev) + 9.0
+    for c in caches:
+        for p in range(wl.P):
+            c.store(p, src_o, src_l, step=0, stream=stream)
+    torch.cuda.synchronize()
+    merge_bytes = wl.merge_bytes()
+    state_bytes = wl.state_bytes()
+
+    def timed(fn, n):
+        for i in range(n_caches):   # warm
+            fn(i)
+        b, e = dita.Event(), dita.Event()
+        b.record(stream)
+        for i in range(n):
+            fn(i % n_caches)
+        e.record(stream)
+        return b.elapsed_ms(e) / n
+
+    def merge(i):
+        c = caches[i]
+        dita.dita_state_merge([c.slot(p)[0] for p in range(wl.P)], [c.slot(p)[1] for p in range(wl.P)],
+                              o=o, lse=lse, stream=stream)
+
+    def copy(i):   # slot 0 of cache i -> slot 1 of cache (i+1): one state read and one written
+        src = caches[i].slot(0)
+        caches[(i + 1) % n_caches].store(1, src[0], src[1], step=1, stream=stream)
+
+    m_ms = min(timed(merge, 4 * n_caches) for _ in range(reps))
+    c_ms = min(timed(copy, 4 * n_caches) for _ in range(reps))
+    m_gbs = merge_bytes / (m_ms / 1e3) / 1e9
+    c_gbs = 2 * state_bytes / (c_ms / 1e3) / 1e9
+    log(f"[bench] isolated: merge {m_ms:.4f} ms = {m_gbs:.0f} GB/s; state copy {c_ms:.4f} ms = {c_gbs:.0f} GB/s")
+    return {
+        "merge": {"ms": m_ms, "bytes": merge_bytes, "GBps": m_gbs, "frac_hbm_peak": m_gbs / PEAK_HBM_GBS},
+        "state_copy": {"ms": c_ms, "bytes": 2 * state_bytes, "GBps": c_gbs,
+                       "frac_hbm_peak": c_gbs / PEAK_HBM_GBS},
+        "note": f"rotating over {n_caches} caches of {wl.P} slots ({n_caches * caches[0].buffer.numel() / 1e9:.2f} GB)",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -262,6 +311,7 @@ def main():
             "avg_launch_ms": sum(merge_ms) / K,
         },
     }
+    result["isolated"] = isolated_bandwidth(dita, wl, tdt, dev, stream, q)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
