@@ -80,6 +80,34 @@ def copy_calibration(nbytes: int):
                                            "write_bytes_per_launch": moved}}), flush=True)
 
 
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the attention and merge kernels from the committed
+    rocprofv3 counter summary, each only while its kernel sources are unchanged
+    since the counters were taken (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload.replace("_bf16", ""))
+    csrc = os.path.join(ROOT, "partial_state_reuse_amd", "csrc")
+    if not os.path.exists(path):
+        return None, None
+
+    def digest(files):
+        h = hashlib.sha256()
+        for f in files:
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+        return h.hexdigest()
+
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("workload") != workload:
+        return None, None
+    attn = rec["attn"]["traffic_bytes_per_launch"] \
+        if rec["attn"]["sources_sha256"] == digest(["attn_bf16.hip", "dita_kernels.h"]) else None
+    merge = rec["merge"]["traffic_bytes_per_launch"] \
+        if rec["merge"]["sources_sha256"] == digest(["merge.hip", "dita_kernels.h"]) else None
+    return attn, merge
+
+
 def upload_parts(x: np.ndarray, wl, dev, tdt):
     import torch
     out = []
@@ -260,6 +288,7 @@ def main():
     achieved = fresh_flops / attn_s / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     merge_gbs = merge_bytes / (sum(merge_ms) / 1e3) / 1e9
+    traffic_attn, traffic_merge = profiled_traffic(wl.name)
     log(f"[bench] timed {K} steps: {total_ms:.3f} ms (host wall {wall * 1e3:.1f} ms); "
         f"attention {sum(attn_ms):.3f} ms, merge {sum(merge_ms):.3f} ms")
 
@@ -299,7 +328,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": traffic_attn,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, calibrated)",
             "launches": launches,
             "avg_launch_ms": attn_s * 1e3 / max(launches, 1),
             "flops_per_launch": fresh_flops / max(launches, 1),
@@ -308,6 +338,7 @@ def main():
             "kernel": "merge_kernel", "bound": "hbm",
             "achieved": merge_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": merge_gbs / PEAK_HBM_GBS, "bytes_per_launch": merge_bytes / K,
+            "traffic": traffic_merge,
             "avg_launch_ms": sum(merge_ms) / K,
         },
     }
