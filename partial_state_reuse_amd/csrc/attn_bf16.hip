@@ -8,52 +8,69 @@
 //
 // Mapping onto CDNA4
 // ------------------
-// * A workgroup owns BM = 4 waves x QB x 32 queries of one (batch, head) and
-//   one fresh partition of a grouped launch.  Workgroup ids are remapped so
-//   that all query tiles of one (head, partition) run on the same XCD and
-//   share its L2 copy of K and V.
-// * K and V tiles (BN keys x D) travel HBM -> LDS with direct-to-LDS buffer
-//   loads (buffer_load_dwordx4 ... lds): no staging registers, per-lane
-//   offsets fixed for the whole kernel, one buffer resource per tile whose
-//   records end at the partition end (rows past it read as zero).  In LDS, K
-//   rows are padded by 16 bytes and V rows by 64 bytes, which keeps both the
-//   K fragment reads and the V transpose reads below free of bank conflicts
-//   while every LDS address is one per-lane base plus an immediate.  Padding
-//   slots are filled from an offset past the buffer end (zeros, no traffic).
-// * Scores are produced transposed, S^T = K Q^T, with
-//   v_mfma_f32_32x32x16_bf16: the A operand is a 32-key x 16-dim slice of the
-//   K tile, the B operand a 32-query Q^T slice held in registers for the
-//   whole kernel.  In the 32x32 accumulator every lane owns ONE query and 16
-//   of the 32 keys; its partner lane (lane ^ 32) owns the other 16.  Each K
-//   fragment read from LDS feeds QB MFMAs (one per 32-query block).
-// * The probabilities feed O^T += V^T P^T directly from registers: for the
-//   B operand a lane supplies 8 keys of its own query, and the 8 accumulator
-//   entries of one half of an S^T block are exactly that (keys {0-3, 8-11}
-//   in the low half-wave, {4-7, 12-15} in the high one).  The matching A
-//   operand (8 keys x one head-dim column of V) comes from two LDS transpose
-//   reads (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element
-//   i%4 of the rows addressed by lanes i/4 + {0,4,8,12}, so pointing lane x
-//   at key (x/4) and head-dim offset 4*(x%4) hands every lane 4 keys of its
-//   own column.  Each V fragment feeds QB MFMAs.
-// * The output accumulator O^T again gives each lane one query, so the
-//   online-softmax rescale and the final 1/l are per-lane scalars.  Rescaling
-//   is lazy: the running max only moves (and O, l are rescaled) when a
-//   tile's max exceeds it by more than 2^8 in the exp2 domain.
-// * Tiles run S, softmax, P V in order; the matrix cores and the VALU overlap
-//   across the two waves that share each SIMD.  (PIPE, a software pipeline
-//   inside each wave -- K one tile ahead of V, the exponentials of tile t
-//   beside the S MFMAs of tile t+1 -- measured slower on gfx950 once QB = 2
-//   halves the LDS traffic per MFMA: it needs a second S buffer, which costs
-//   the second wave per SIMD.)  Measured on the 75,600-token shape: QB=2 and
-//   no pipeline 1.03 PFLOP/s, QB=1 with pipeline 0.97, QB=2 with pipeline 0.71.
-// * The denominator sums the fp32 probabilities (LSE keeps fp32 accuracy);
-//   the P V product uses them rounded to bf16.
+// * A workgroup owns 512 queries (8 waves x 2 blocks of 32) of one (batch,
+//   head) and one fresh partition of a grouped launch.  Workgroup ids are
+//   remapped so that all query tiles of one (head, partition) run on the same
+//   XCD and share its L2 copy of K and V.
+// * Ping-pong: the waves form two groups of four (A = waves 0-3, B = 4-7; one
+//   wave of each group per SIMD).  Each group alternates an MFMA phase (P V of
+//   tile t-1, then S of tile t) with a softmax phase (exponentials of tile t);
+//   B runs one phase behind A and a workgroup barrier separates phases, so on
+//   every SIMD one wave keeps the matrix core busy while the other issues the
+//   softmax VALU work.  (A lone wave issues a VALU instruction only every ~6-10
+//   cycles on gfx950, so the softmax of a tile takes about as long as its 32
+//   MFMAs; left unsynchronised, the two waves of a SIMD drift into the same
+//   phase.)
+// * Scores are produced transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//   the A operand is a 32-key x 16-dim slice of the K tile, the B operand a
+//   32-query Q^T slice held in registers for the whole kernel.  In the 32x32
+//   accumulator every lane owns ONE query and 16 of the 32 keys; its partner
+//   lane (lane ^ 32) owns the other 16.  Each K fragment feeds both query
+//   blocks of the wave.
+// * The probabilities feed O^T += V^T P^T directly from registers: for the B
+//   operand a lane supplies 8 keys of its own query, and the 8 accumulator
+//   entries of one half of an S^T block are exactly that (keys {0-3, 8-11} in
+//   the low half-wave, {4-7, 12-15} in the high one).  The matching A operand
+//   (8 keys x one head-dim column of V) comes from two LDS transpose reads
+//   (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element i%4
+//   of the rows addressed by lanes i/4 + {0,4,8,12}, so pointing lane x at key
+//   (x/4) and head-dim offset 4*(x%4) hands every lane 4 keys of its own
+//   column.  Each V fragment feeds both query blocks.
+// * An MFMA phase is a static schedule of 16 steps (8 P V groups, 8 S k-steps);
+//   LDS reads run three steps ahead with explicit lgkmcnt waits.
+// * K and V tiles (32 keys x D for D = 128) travel HBM -> LDS with
+//   direct-to-LDS buffer loads through a five-stage ring; stage s holds K tile
+//   s and V tile s-1, the two operands of MFMA phase s.  (Five, not four: stage
+//   t must stay intact through group B's softmax phase of step t, whose rare
+//   exact path re-reads K tile t while group A already fetches stage t+4.)  A
+//   vector memory instruction occupies the CU's address unit for tens of cycles
+//   and stalls its wave meanwhile, so each wave issues its share of a stage
+//   spread over both of its phases (one load at a per-wave step of the MFMA
+//   phase, the rest between the query blocks of the softmax phase), two tiles
+//   ahead of use.  In LDS, K rows are padded by 16 bytes and V rows by 64
+//   bytes, which keeps the K fragment reads and the V transpose reads free of
+//   bank conflicts while every LDS address is one per-lane base plus an
+//   immediate.
+//   Padding slots, rows past the partition end and tiles past the last one are
+//   loaded through buffer resources whose records end there (zeros, no memory
+//   access).
+// * The output accumulator O^T gives each lane one query, so the rescale and
+//   the final 1/l are per-lane scalars.  The first tile takes the exact
+//   running max; later tiles exponentiate against the running max directly and
+//   take the exact max / rescale path (scores recomputed from the K tile still
+//   in LDS) only when some lane's partial sum exceeds 2^16, i.e. when a score
+//   rose well above the running max.  The denominator sums the fp32
+//   probabilities (LSE keeps fp32 accuracy); P V uses them rounded to bf16.
 // * Ragged tails: query rows past Nq load a clamped row and are not stored;
 //   key rows past nk read as zero and their scores are set to -inf.
+//
+// Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.12
+// PFLOP/s, against 1.08 for a four-wave kernel without phase synchronisation.
 
 #include "dita_kernels.h"
 
 #include <cmath>
+#include <utility>
 
 namespace dita {
 namespace {
@@ -63,12 +80,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the running max
+constexpr float kFastLimit = 65536.0f; // largest per-lane partial sum the fast path accepts
 constexpr int kXcds = 8;
 
 __device__ inline u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -90,10 +107,66 @@ __device__ inline int64_t xcd_remap(int64_t pid, int64_t n) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-template <int D, int QB>
+// LDS reads issued through inline assembly.  The compiler treats the
+// ds_read_b64_tr_b16 builtin as possibly aliasing any pending direct-to-LDS
+// buffer load and waits for every outstanding load (the prefetch of later
+// stages included) before it; the kernel orders its LDS fills itself (vmcnt
+// wait plus barrier before a stage is read), so the reads are issued here and
+// their completion is awaited explicitly.  LDS operations complete in order,
+// so lgkmcnt(N) with N counting only these reads is exact or waits longer.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+template <int OFF>
+__device__ inline s16x4 tr_read(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ inline u32x4 k_read(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// Wait until at most N LDS operations are outstanding; the fragments are passed
+// through so that their consumers cannot be scheduled above the wait.
+template <int N>
+__device__ inline void lgkm_wait(s16x4& a, s16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ inline void lgkm_wait1(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+// LDS reads still outstanding, in a schedule of steps with PF steps in flight,
+// once step i's reads are needed: the reads of steps i+1 .. i+PF-1 (steps below
+// NPV issue two reads, the others one).
+template <int NPV, int LAST, int PF>
+constexpr int pending_reads(int i) {
+  int n = 0;
+  for (int j = i + 1; j <= i + PF - 1 && j < LAST; ++j) n += j < NPV ? 2 : 1;
+  return n;
+}
+
+template <int I>
+struct Int { static constexpr int value = I; };
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(Int<I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int D>
 struct Tile {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
+  static constexpr int QB = 2;                       // 32-query blocks per wave
   static constexpr int BM = kWaves * 32 * QB;        // queries per workgroup
   static constexpr int BN = 4096 / D;                // keys per tile: 32 (D=128), 64 (D=64)
   static constexpr int ROW_BYTES = D * 2;            // one K or V row in HBM
@@ -102,14 +175,15 @@ struct Tile {
   static constexpr int VS = ROW_BYTES + 64;          // V row stride in LDS
   static constexpr int K_SPR = KS / 16;              // 16-byte LDS slots per K row
   static constexpr int V_SPR = VS / 16;
-  static constexpr int K_REGION = (BN * KS + 1023) / 1024 * 1024;  // whole wave loads
+  static constexpr int K_REGION = (BN * KS + 1023) / 1024 * 1024;  // whole wave-loads
   static constexpr int V_REGION = (BN * VS + 1023) / 1024 * 1024;
   static constexpr int K_WLOADS = K_REGION / 1024;   // wave-wide 16-byte loads per K tile
   static constexpr int V_WLOADS = V_REGION / 1024;
-  static constexpr int K_PER_WAVE = (K_WLOADS + kWaves - 1) / kWaves;
-  static constexpr int V_PER_WAVE = (V_WLOADS + kWaves - 1) / kWaves;
+  static constexpr int WLOADS = K_WLOADS + V_WLOADS;  // per stage, dealt over the 8 waves
   static constexpr int TILE_BYTES = BN * ROW_BYTES;  // bytes of one tile in HBM
-  static constexpr int LDS_BYTES = 2 * K_REGION + 2 * V_REGION;
+  static constexpr int STAGE = K_REGION + V_REGION;
+  static constexpr int NSTAGE = 5;
+  static_assert(WLOADS <= 24, "a wave's share of a stage is at most three loads");
 };
 
 // Byte offset, inside a tile in HBM, that fills LDS slot `slot` of a region
@@ -120,25 +194,10 @@ __device__ inline uint32_t slot_offset(int slot, int spr, int rows, int cpr, int
   return (row < rows && col < cpr) ? uint32_t(row * row_bytes + col * 16) : 0x7ffffff0u;
 }
 
-// One tile HBM -> LDS: wave w issues wave-loads w, w + 4, ...; wave-load i fills
-// LDS slots [64 i, 64 i + 64) of `region` (lane-linear), lane data from off[j].
-// (A plain device function: the buffer-resource builtins inside a lambda make
-// the host pass drop the kernel's launch stub.)
-template <int PER_WAVE, int WLOADS>
-__device__ inline void load_region(__amdgpu_buffer_rsrc_t r, char* region, int wave,
-                                   const uint32_t* off) {
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int i = wave + 4 * j;
-    if (i < WLOADS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(region + i * 1024), 16, off[j], 0, 0, 0);
-  }
-}
-
 // Buffer resource over tile t of one head's K or V: records end at the
-// partition end, so rows past nk read as zero.  Every field is made
-// explicitly wave-uniform (a resource the compiler cannot prove uniform turns
-// each load into a read-first-lane loop).
+// partition end, so rows past nk (and every tile at or past the last one) read
+// as zero.  Every field is made explicitly wave-uniform (a resource the
+// compiler cannot prove uniform turns each load into a read-first-lane loop).
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* head, int t, int tile_bytes,
                                                    uint32_t head_bytes) {
   const uint32_t start = uint32_t(t) * uint32_t(tile_bytes);
@@ -151,34 +210,78 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* head, int t, int 
                                            0x00020000);
 }
 
+// Load J (0, 1, 2) of a wave's share of stage s: the stage's wave-loads
+// (K tile s, then V tile s-1) are dealt round-robin over the eight waves, so
+// wave w issues wave-loads w, w + 8, w + 16.  Stage 0 has no V tile: its V
+// loads use the empty tile past the end, so every wave issues the same number
+// of loads for every stage.  (A plain device function: buffer-resource
+// builtins inside a kernel lambda make the host pass drop the launch stub.)
+template <typename T, int J>
+__device__ inline void load_share_item(char* smem, int s, int ntiles, const char* k_head,
+                                       const char* v_head, uint32_t head_bytes, int wave,
+                                       int lane) {
+  // Opaque copy of the lane index: the offsets are recomputed at every call
+  // instead of being hoisted out of the tile loop into registers it cannot spare.
+  asm volatile("" : "+v"(lane));
+  char* base = smem + (s % T::NSTAGE) * T::STAGE;
+  const int k = wave + 8 * J;
+  if (k < T::K_WLOADS) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_head, s, T::TILE_BYTES, head_bytes);
+    const uint32_t off = slot_offset(k * 64 + lane, T::K_SPR, T::BN, T::CPR, T::ROW_BYTES);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(base + k * 1024), 16, off, 0, 0, 0);
+  } else if (k < T::WLOADS) {
+    const __amdgpu_buffer_rsrc_t rv =
+        tile_rsrc(v_head, s >= 1 ? s - 1 : ntiles, T::TILE_BYTES, head_bytes);
+    const int i = k - T::K_WLOADS;
+    const uint32_t off = slot_offset(i * 64 + lane, T::V_SPR, T::BN, T::CPR, T::ROW_BYTES);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + T::K_REGION + i * 1024), 16,
+                                             off, 0, 0, 0);
+  }
+}
 template <typename T>
-__device__ inline void load_k_tile(const char* head, int t, uint32_t head_bytes, char* region,
-                                   int wave, const uint32_t* off) {
-  load_region<T::K_PER_WAVE, T::K_WLOADS>(tile_rsrc(head, t, T::TILE_BYTES, head_bytes), region,
-                                          wave, off);
+__device__ inline void load_share(char* smem, int s, int ntiles, const char* k_head,
+                                  const char* v_head, uint32_t head_bytes, int wave, int lane) {
+  load_share_item<T, 0>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
+  load_share_item<T, 1>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
+  load_share_item<T, 2>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
 }
 
-template <typename T>
-__device__ inline void load_v_tile(const char* head, int t, uint32_t head_bytes, char* region,
-                                   int wave, const uint32_t* off) {
-  load_region<T::V_PER_WAVE, T::V_WLOADS>(tile_rsrc(head, t, T::TILE_BYTES, head_bytes), region,
-                                          wave, off);
+// vmcnt waits.  A wave issues n = (WLOADS - wave + 7) / 8 loads per stage; the
+// waits below leave exactly the loads of later stages in flight.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
+}
+template <typename T, int STAGES, int EXTRA>
+__device__ inline void wait_stages_in_flight(int wave) {
+  constexpr int LO = T::WLOADS / 8, R = T::WLOADS % 8;
+  if (wave < R)
+    wait_vm<(LO + 1) * STAGES + EXTRA>();
+  else
+    wait_vm<LO * STAGES + EXTRA>();
+}
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroup barrier without a memory fence: LDS contents are ordered by the
+// explicit vmcnt waits of the waves that loaded them.
+__device__ inline void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <int D, int QB, bool PIPE>
-__global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_kernel(
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int QT, float scale_log2) {
-  using T = Tile<D, QB>;
-  constexpr int NB = T::BN / 32;   // 32-key blocks per tile
-  constexpr int NKK = D / 16;      // MFMA k-steps over the head dim
-  constexpr int ND = D / 32;       // 32-wide blocks of the head dim
+  using T = Tile<D>;
+  constexpr int QB = T::QB;
+  constexpr int NB = T::BN / 32;
+  constexpr int NKK = D / 16;
+  constexpr int ND = D / 32;
 
-  // K stage 0, K stage 1, V stage 0, V stage 1.
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
 
-  // Workgroup-uniform decode of the tile id (made explicit: integer division is
-  // expanded into vector instructions, and values derived from it would
-  // otherwise be treated as per-lane).
   const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(blockIdx.x, int64_t(gridDim.x))));
   const int qt = __builtin_amdgcn_readfirstlane(lin % QT);
   const int rest = __builtin_amdgcn_readfirstlane(lin / QT);
@@ -189,6 +292,8 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wl = wave & 3;
   const int m32 = lane & 31;
   const int hh = lane >> 5;
   const int nk = int(job.nk);
@@ -197,21 +302,6 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
   const uint32_t head_bytes = uint32_t(nk) * T::ROW_BYTES;
   const char* k_head = reinterpret_cast<const char*>(job.k) + bh * int64_t(head_bytes);
   const char* v_head = reinterpret_cast<const char*>(job.v) + bh * int64_t(head_bytes);
-  uint32_t k_off[T::K_PER_WAVE], v_off[T::V_PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < T::K_PER_WAVE; ++j)
-    k_off[j] = slot_offset((wave + 4 * j) * 64 + lane, T::K_SPR, T::BN, T::CPR, T::ROW_BYTES);
-#pragma unroll
-  for (int j = 0; j < T::V_PER_WAVE; ++j)
-    v_off[j] = slot_offset((wave + 4 * j) * 64 + lane, T::V_SPR, T::BN, T::CPR, T::ROW_BYTES);
-  char* const k_stage0 = smem;
-  char* const v_stage0 = smem + 2 * T::K_REGION;
-
-  load_k_tile<T>(k_head, 0, head_bytes, k_stage0, wave, k_off);
-  if (PIPE && ntiles > 1) load_k_tile<T>(k_head, 1, head_bytes, k_stage0 + T::K_REGION, wave, k_off);
-  load_v_tile<T>(v_head, 0, head_bytes, v_stage0, wave, v_off);
-
-  // Q^T operand: for query block qb, lane holds Q[row][kk*16 + 8*hh .. +7].
   const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
   int qrow[QB];
   bf16x8 qf[QB][NKK];
@@ -223,19 +313,17 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
     for (int kk = 0; kk < NKK; ++kk)
       qf[qb][kk] = as_bf16x8(load16(qp + int64_t(qrow_c) * D + kk * 16 + 8 * hh));
   }
+#pragma unroll
+  for (int st0 = 0; st0 < 3; ++st0)
+    load_share<T>(smem, st0, ntiles, k_head, v_head, head_bytes, wave, lane);
 
-  // Per-lane LDS read offsets; everything else is a compile-time immediate.
-  //   K fragment (block b, k-step kk): row 32b + m32, bytes [32kk + 16hh, +16).
-  //   V transpose read (block b, half h2, read r2, head-dim block d): lane x of a
-  //   16-lane group addresses row 32b + 16h2 + 8r2 + 4hh + x/4, head-dim
-  //   32d + 16gh + 4(x%4), four elements.
   const int k_lane = m32 * T::KS + 16 * hh;
   const int g16 = lane & 15;
   const int gh = (lane >> 4) & 1;
   const int v_lane = (4 * hh + (g16 >> 2)) * T::VS + 32 * gh + 8 * (g16 & 3);
 
   f32x16 oacc[QB][ND];
-  float m_run[QB], l_run[QB];  // running max (exp2 domain), lane's partial denominator
+  float m_run[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -261,7 +349,6 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
           s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kk], s[qb][b], 0, 0, 0);
       }
   };
-  // Keys past the partition end score -inf (only the last tile has any).
   auto mask_tail = [&](int t, f32x16 (*s)[NB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -284,135 +371,238 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
       mx[qb] = m;
     }
   };
-  // P = exp2(S * scale*log2e - m): fp32 into the denominator, bf16 for P V.
+  // Exponentials of one query block against the running max, fp32 sum into
+  // the lane's partial denominator, bf16 copies for P V.
+  auto softmax_qb = [&](int qb, const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 v;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + j], scale_log2, -m_run[qb]));
+          part += e;
+          v[j] = (__bf16)e;
+        }
+        l_run[qb] += part;
+        pb[qb][b][h2] = v;
+      }
+  };
   auto softmax = [&](const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) softmax_qb(qb, s, pb);
+  };
+  auto pv = [&](const char* vreg, bf16x8 (*pb)[NB][2]) {
+    constexpr int G = NB * 2 * ND;
+    const uint32_t va = lds_addr(vreg + v_lane);
+    s16x4 fr[G][2];
+    auto issue = [&](auto gi) {
+      constexpr int g = decltype(gi)::value;
+      constexpr int b = g / (2 * ND), h2 = (g / ND) % 2, d = g % ND;
+      fr[g][0] = tr_read<(32 * b + 16 * h2) * T::VS + 64 * d>(va);
+      fr[g][1] = tr_read<(32 * b + 16 * h2 + 8) * T::VS + 64 * d>(va);
+    };
+    issue(Int<0>{});
+    issue(Int<1>{});
+    static_for<G>([&](auto gi) {
+      constexpr int g = decltype(gi)::value;
+      constexpr int b = g / (2 * ND), h2 = (g / ND) % 2, d = g % ND;
+      lgkm_wait<(g + 1 < G) ? 2 : 0>(fr[g][0], fr[g][1]);
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(fr[g][0], fr[g][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][b][h2], oacc[qb][d], 0, 0, 0);
+      if constexpr (g + 2 < G) issue(Int<g + 2>{});
+    });
+  };
+  auto rescale_qb = [&](int qb, float mxq) {
+    const float m = fmaxf(mxq, __shfl_xor(mxq, 32));
+    const float m_new = fmaxf(m_run[qb], m * scale_log2);
+    if (__any(m_new > m_run[qb] + kRescaleSlack)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[qb][d][i] *= alpha;
+      m_run[qb] = m_new;
+    }
+  };
+  auto rescale = [&](const float* mx) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) rescale_qb(qb, mx[qb]);
+  };
+  // Exponentials against the running max, without a tile max (after the first
+  // tile the running max is finite).  Returns false, leaving l untouched, if
+  // some lane's partial sum exceeds 2^16 or is not finite; the caller then
+  // takes the exact max / rescale path.  Masked keys (-inf) give exactly 0 on
+  // either path.  `between(qb)` runs before each query block (load issue).
+  auto softmax_fast = [&](const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2], auto&& between) -> bool {
+    float part[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      between(qb);
+      part[qb] = 0.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           bf16x8 v;
-          float part = 0.0f;
+          float p2 = 0.0f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float e =
                 __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + j], scale_log2, -m_run[qb]));
-            part += e;
+            p2 += e;
             v[j] = (__bf16)e;
           }
-          l_run[qb] += part;
+          part[qb] += p2;
           pb[qb][b][h2] = v;
         }
-  };
-  // O^T += V^T P^T; the V^T operand comes from two transpose reads per MFMA
-  // group.  Consecutive MFMAs go to different accumulators.
-  auto pv = [&](const char* vreg, bf16x8 (*pb)[NB][2]) {
-    const char* vb0 = vreg + v_lane;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          s16x4 part[2];
-#pragma unroll
-          for (int r2 = 0; r2 < 2; ++r2)
-            part[r2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(vb0 + (32 * b + 16 * h2 + 8 * r2) * T::VS + 64 * d));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][b][h2], oacc[qb][d], 0, 0, 0);
-        }
-  };
-  auto rescale = [&](const float* mx) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m = fmaxf(mx[qb], __shfl_xor(mx[qb], 32));
-      const float m_new = fmaxf(m_run[qb], m * scale_log2);
-      if (__any(m_new > m_run[qb] + kRescaleSlack)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qb][d][i] *= alpha;
-        m_run[qb] = m_new;
-      }
     }
+    bool ok = true;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) ok = ok && (part[qb] <= kFastLimit);
+    const bool all_ok = !__any(!ok);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += all_ok ? part[qb] : 0.0f;
+    return all_ok;
   };
 
-  if constexpr (PIPE) {
-    // Start of tile t: wait for K_{t+1} and V_t, free the stages of K_t and
-    // V_{t-1}, prefetch K_{t+2} and V_{t+1}, apply the tail mask, update the max.
-    auto head = [&](int t, f32x16 (*sc)[NB], float* mx) {
-      __builtin_amdgcn_s_waitcnt(0);  // this thread's K_{t+1} and V_t have landed
-      __syncthreads();                // ... everyone's; K_t and V_{t-1} are no longer read
-      if (t + 2 < ntiles)
-        load_k_tile<T>(k_head, t + 2, head_bytes, k_stage0 + (t & 1) * T::K_REGION, wave, k_off);
-      if (t + 1 < ntiles)
-        load_v_tile<T>(v_head, t + 1, head_bytes, v_stage0 + ((t + 1) & 1) * T::V_REGION, wave,
-                       v_off);
-      if ((t + 1) * T::BN > nk) {
-        mask_tail(t, sc);
-        row_max(sc, mx);
+  // One MFMA phase as a static schedule of steps: steps [0, NPV) are the P V
+  // groups of the previous tile (two transpose reads, QB MFMAs each), steps
+  // [NPV, NPV + NS) the S k-steps of this tile (one K read, QB MFMAs each).
+  // Reads run PF steps ahead of their MFMAs.
+  constexpr int NPV = NB * 2 * ND;
+  constexpr int NS = NB * NKK;
+  constexpr int PF = 3;
+  auto m_phase = [&](auto first_c, auto last_c, const char* stg, f32x16 (*s)[NB],
+                     bf16x8 (*pb)[NB][2], int load_stage_idx) {
+    constexpr int FIRST = decltype(first_c)::value;
+    constexpr int LAST = decltype(last_c)::value;
+    const uint32_t va = lds_addr(stg + T::K_REGION + v_lane);
+    const uint32_t ka = lds_addr(stg + k_lane);
+    s16x4 fr[NPV][2];
+    u32x4 kf[NS];
+    auto issue = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i < NPV) {
+        constexpr int b = i / (2 * ND), h2 = (i / ND) % 2, d = i % ND;
+        fr[i][0] = tr_read<(32 * b + 16 * h2) * T::VS + 64 * d>(va);
+        fr[i][1] = tr_read<(32 * b + 16 * h2 + 8) * T::VS + 64 * d>(va);
+      } else {
+        constexpr int j = i - NPV, b = j / NKK, kk = j % NKK;
+        kf[j] = k_read<b * 32 * T::KS + 32 * kk>(ka);
       }
-      rescale(mx);
     };
-
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 sc[QB][NB];
-    float mx[QB];
-    compute_s(k_stage0, sc);
-    row_max(sc, mx);
-
-    // Tiles with a successor: the exponentials of tile t beside the S MFMAs of
-    // tile t+1, the P V MFMAs of tile t beside the row max of tile t+1.
-    int t = 0;
-    for (; t + 1 < ntiles; ++t) {
-      head(t, sc, mx);
-      bf16x8 pb[QB][NB][2];
-      f32x16 sn[QB][NB];
-      softmax(sc, pb);
-      compute_s(k_stage0 + ((t + 1) & 1) * T::K_REGION, sn);
-      pv(v_stage0 + (t & 1) * T::V_REGION, pb);
-      row_max(sn, mx);
+    static_for<PF>([&](auto c) {
+      constexpr int i = FIRST + decltype(c)::value;
+      if constexpr (i < LAST) issue(Int<i>{});
+    });
+    static_for<LAST - FIRST>([&](auto c) {
+      constexpr int i = FIRST + decltype(c)::value;
+      constexpr int pend = pending_reads<NPV, LAST, PF>(i);
+      if constexpr (i < NPV) {
+        constexpr int b = i / (2 * ND), h2 = (i / ND) % 2, d = i % ND;
+        lgkm_wait<pend>(fr[i][0], fr[i][1]);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(fr[i][0], fr[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][b][h2], oacc[qb][d], 0, 0, 0);
+      } else {
+        constexpr int j = i - NPV, b = j / NKK, kk = j % NKK;
+        lgkm_wait1<pend>(kf[j]);
+        const bf16x8 a = as_bf16x8(kf[j]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) sc[qb][b] = sn[qb][b];
-    }
-    {
-      head(t, sc, mx);
-      bf16x8 pb[QB][NB][2];
-      softmax(sc, pb);
-      pv(v_stage0 + (t & 1) * T::V_REGION, pb);
-    }
-  } else {
-    // K_t and V_t share stage t % 2; the next tile is fetched while this one computes.
-    for (int t = 0; t < ntiles; ++t) {
-      __builtin_amdgcn_s_waitcnt(0);  // this thread's K_t and V_t have landed
-      __syncthreads();                // ... everyone's; tile t-1's stage is free
-      if (t + 1 < ntiles) {
-        load_k_tile<T>(k_head, t + 1, head_bytes, k_stage0 + ((t + 1) & 1) * T::K_REGION, wave,
-                       k_off);
-        load_v_tile<T>(v_head, t + 1, head_bytes, v_stage0 + ((t + 1) & 1) * T::V_REGION, wave,
-                       v_off);
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kk],
+                                                             kk == 0 ? zero16() : s[qb][b], 0, 0, 0);
       }
-      f32x16 sc[QB][NB];
-      float mx[QB];
-      compute_s(k_stage0 + (t & 1) * T::K_REGION, sc);
+      if constexpr (i + PF < LAST) issue(Int<i + PF>{});
+      // Item 0 of this wave's share of stage load_stage_idx, at a step that
+      // differs per wave of the group (staggered use of the address unit).
+      if constexpr ((i - FIRST) % 4 == 1 && (i - FIRST) / 4 < 4) {
+        if (load_stage_idx >= 0 && wl == (i - FIRST) / 4)
+          load_share_item<T, 0>(smem, load_stage_idx, ntiles, k_head, v_head, head_bytes, wave, lane);
+      }
+      // Keep the written order: each step's MFMAs before the next step's wait.
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Phase schedule (group A = waves 0-3, B = waves 4-7):
+  //   A: M(0) V(0) M(1) V(1) ... M(T)      B: -- M(0) V(0) ... V(T-1) M(T)
+  // M(t) = P V of tile t-1 and S of tile t, reading stage t; V(t) = softmax of
+  // tile t.  Every wave fetches its share of stage t+3 during M(t) (one load,
+  // at a step that differs per wave) and V(t) (the rest), and its share of
+  // stage s has landed by the end of phase 2s-1: group A waits at the end of
+  // V(s-1) with stages s+1, s+2 still in flight, group B at the end of M(s-1)
+  // with stage s+1 and one load of stage s+2 in flight.
+  wait_stages_in_flight<T, 2, 0>(wave);  // stage 0 (stages 1, 2 in flight)
+  phase_barrier();
+  if (grp == 1) phase_barrier();
+  f32x16 sc[QB][NB];
+  bf16x8 pb[QB][NB][2];
+  if (ntiles > 0) {  // step 0: S only, exact max
+    __builtin_amdgcn_s_setprio(1);
+    m_phase(Int<NPV>{}, Int<NPV + NS>{}, smem, sc, pb, 3);
+    if (wl >= 2) load_share_item<T, 0>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) wait_stages_in_flight<T, 1, 1>(wave);
+    phase_barrier();
+    load_share_item<T, 1>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    load_share_item<T, 2>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    if (T::BN > nk) mask_tail(0, sc);
+    float mx[QB];
+    row_max(sc, mx);
+    rescale(mx);
+    softmax(sc, pb);
+    if (grp == 0) wait_stages_in_flight<T, 2, 0>(wave);
+    phase_barrier();
+  }
+  for (int t = 1; t < ntiles; ++t) {
+    const char* st = smem + (t % T::NSTAGE) * T::STAGE;
+    __builtin_amdgcn_s_setprio(1);
+    m_phase(Int<0>{}, Int<NPV + NS>{}, st, sc, pb, t + 3);
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 1) wait_stages_in_flight<T, 1, 1>(wave);
+    phase_barrier();
+
+    if ((t + 1) * T::BN > nk) mask_tail(t, sc);
+    auto loads_between = [&](int qb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == (wl & 1))
+        load_share_item<T, 1>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const bool fast = softmax_fast(sc, pb, loads_between);
+    __builtin_amdgcn_sched_barrier(0);
+    load_share_item<T, 2>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!fast) {
+      // The fast path consumed the scores: recompute them from the K tile.
+      compute_s(smem + (t % T::NSTAGE) * T::STAGE, sc);
       if ((t + 1) * T::BN > nk) mask_tail(t, sc);
+      float mx[QB];
       row_max(sc, mx);
       rescale(mx);
-      bf16x8 pb[QB][NB][2];
       softmax(sc, pb);
-      pv(v_stage0 + (t & 1) * T::V_REGION, pb);
     }
+    if (grp == 0) wait_stages_in_flight<T, 2, 0>(wave);
+    phase_barrier();
   }
+  if (ntiles > 0) {
+    __builtin_amdgcn_s_setprio(1);
+    m_phase(Int<0>{}, Int<NPV>{}, smem + (ntiles % T::NSTAGE) * T::STAGE, sc, pb, -1);
+    __builtin_amdgcn_s_setprio(0);
+  }
+  if (grp == 0) phase_barrier();
+  wait_loads();  // the zero-filling loads past the last stage must land before LDS is released
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -434,18 +624,13 @@ __global__ __launch_bounds__(256, (QB == 2 && PIPE) ? 1 : 2) void attn_fwd_bf16_
   }
 }
 
-// Tile configuration of the launch: QB query blocks of 32 per wave, and
-// whether tiles are software-pipelined inside the wave.
-constexpr int kQB = 2;
-constexpr bool kPipe = false;
-
 template <int D>
 hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                     hipStream_t stream) {
-  using T = Tile<D, kQB>;
+  using T = Tile<D>;
   const int QT = int((pr.Nq + T::BM - 1) / T::BM);
   const int64_t n = int64_t(QT) * pr.BH * n_jobs;
-  attn_fwd_bf16_kernel<D, kQB, kPipe><<<dim3(unsigned(n)), T::kThreads, 0, stream>>>(
+  attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), T::kThreads, 0, stream>>>(
       static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, QT, pr.scale * kLog2e);
   return hipGetLastError();
 }
