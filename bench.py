@@ -17,8 +17,16 @@ roofline of the dominant kernel (the fresh-attention launch, timed with HIP
 events on its own stream), the merge's bandwidth, and the fp64 CPU oracle
 timed on a bounded sample of the same step.
 
+With --trajectory the schedule also runs once from a cold cache beside an
+all-fresh reference computed by the same library on the same K/V (every
+partition recomputed, which equals full attention): per step the fresh
+blocks, the step latency, the max-abs and relative-Frobenius error of the
+reused output against the all-fresh one (and its running max), and the
+contribution of each partition to the output by distance from the local one
+(mean over rows of exp(LSE_p - LSE) at the all-fresh step 0).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--seed S]
+                       [--no-cpu-baseline] [--seed S] [--trajectory]
 """
 
 from __future__ import annotations
@@ -52,6 +60,9 @@ def parse():
     ap.add_argument("--workload", default="dit75k_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trajectory", action="store_true",
+                    help="also run the whole schedule once from a cold cache beside an all-fresh "
+                         "reference and report per-step error, fresh blocks and latency")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--resident-steps", type=int, default=0,
                     help="distinct K/V steps to generate (0: the whole schedule); step s uses "
@@ -117,6 +128,26 @@ def upload_parts(x: np.ndarray, wl, dev, tdt):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        return [{k: d.get(k) for k in ("internal_api", "num_threads", "version")}
+                for d in threadpool_info()]
+    except Exception:
+        return []
+
+
 def cpu_baseline(inp, wl, budget_s: float):
     """The fp64 oracle's rank-step, timed as it stands on the host cores, on a head
     sample of a non-anchor step (fresh blocks + P-way merge)."""
@@ -151,11 +182,14 @@ def cpu_baseline(inp, wl, budget_s: float):
         heads_done += 1
         if elapsed >= budget_s:
             break
+    host = {"affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+            "blas": _blas_info()}
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "host": host,
         "ms_per_step": elapsed / heads_done * wl.H * 1e3,
         "sample": (f"fp64 numpy oracle rank-step (schedule step {s % wl.steps}: "
                    f"{int((mask == 0).sum())} fresh blocks + {wl.P}-way merge) on {heads_done} of "
@@ -210,6 +244,65 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
                        "frac_hbm_peak": c_gbs / PEAK_HBM_GBS},
         "note": f"rotating over {n_caches} caches of {wl.P} slots ({n_caches * caches[0].buffer.numel() / 1e9:.2f} GB)",
     }
+
+
+def trajectory(dita, wl, seed, dev, tdt, stream):
+    """The schedule once from a cold cache beside an all-fresh reference (same library,
+    same K/V, every partition recomputed): per-step error of the reused output, fresh
+    blocks, step latency, and the contribution profile by partition distance."""
+    import torch
+    from workloads import Inputs
+    inp = Inputs(wl, seed=seed)
+    q = torch.from_numpy(inp.q).to(tdt).to(dev)
+    cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
+    ref = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
+    plan = dita.Plan(**wl.plan_fields())
+    shape = (wl.B, wl.H, wl.Nq, wl.D)
+    o = torch.empty(shape, dtype=tdt, device=dev)
+    o_ref = torch.empty(shape, dtype=tdt, device=dev)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    lse_ref = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    all_fresh = np.zeros(wl.P, dtype=np.uint8)
+    out = {"fresh": [], "step_ms": [], "err_max_abs": [], "err_rel_fro": [], "lse_err_max_abs": []}
+    contribution = None
+    for s in range(wl.steps):
+        k, v = inp.kv(s)
+        ks, vs = upload_parts(k, wl, dev, tdt), upload_parts(v, wl, dev, tdt)
+        del k, v
+        mask = dita.dita_plan_mask(plan, s, cache)
+        ev = (dita.Event(), dita.Event(), dita.Event())
+        _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, s, o=o, lse=lse, stream=stream,
+                                         events=(ev[0].handle, ev[1].handle, ev[2].handle))
+        dita.dita_attn_step(ref, q, ks, vs, all_fresh, s, o=o_ref, lse=lse_ref, stream=stream)
+        torch.cuda.synchronize()
+        d = o.float() - o_ref.float()
+        out["fresh"].append(int(info.n_fresh))
+        out["step_ms"].append(round(ev[0].elapsed_ms(ev[2]), 4))
+        out["err_max_abs"].append(float(d.abs().max()))
+        out["err_rel_fro"].append(float(torch.linalg.vector_norm(d) /
+                                        torch.linalg.vector_norm(o_ref.float())))
+        out["lse_err_max_abs"].append(float((lse - lse_ref).abs().max()))
+        if s == 0:
+            contribution = []
+            for p in range(wl.P):
+                _, lse_p = ref.slot(p)
+                contribution.append(float(torch.exp(lse_p - lse_ref).mean()))
+        log(f"[bench] trajectory step {s}: fresh {info.n_fresh}/{wl.P}  "
+            f"err max-abs {out['err_max_abs'][-1]:.3e}  rel-Fro {out['err_rel_fro'][-1]:.3e}")
+        del ks, vs
+    run = 0.0
+    out["err_running_max"] = []
+    for e in out["err_max_abs"]:
+        run = max(run, e)
+        out["err_running_max"].append(run)
+    out["fresh_blocks"] = sum(out["fresh"])
+    out["fresh_fraction"] = out["fresh_blocks"] / (wl.steps * wl.P)
+    out["contribution_by_distance"] = [
+        {"distance": abs(p - wl.q_part), "partition": p, "mean_weight": contribution[p]}
+        for p in range(wl.P)]
+    out["reference"] = ("all-fresh step through the same library on the same K/V "
+                        "(every partition recomputed = full attention)")
+    return out
 
 
 def main():
@@ -320,6 +413,8 @@ def main():
         "attn_ms_per_step": sum(attn_ms) / K,
         "merge_ms_per_step": sum(merge_ms) / K,
         "step_ms": [round(x, 4) for x in step_ms],
+        "step_ms_median": float(np.median(step_ms)),
+        "step_ms_min": float(np.min(step_ms)),
         "roofline": {
             "kernel": "attn_fwd_bf16_kernel (grouped fresh partial attention)"
             if wl.dtype == "bf16" else "attn_fwd_f32_kernel",
@@ -343,6 +438,11 @@ def main():
         },
     }
     result["isolated"] = isolated_bandwidth(dita, wl, tdt, dev, stream, q)
+    if args.trajectory:
+        del kv, cache
+        torch.cuda.empty_cache()
+        log("[bench] trajectory: the schedule from a cold cache beside an all-fresh reference")
+        result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
