@@ -44,16 +44,16 @@
 //   t must stay intact through group B's softmax phase of step t, whose rare
 //   exact path re-reads K tile t while group A already fetches stage t+4.)  A
 //   vector memory instruction occupies the CU's address unit for tens of cycles
-//   and stalls its wave meanwhile, so each wave issues its share of a stage
-//   spread over both of its phases (one load at a per-wave step of the MFMA
-//   phase, the rest between the query blocks of the softmax phase), two tiles
-//   ahead of use.  In LDS, K rows are padded by 16 bytes and V rows by 64
-//   bytes, which keeps the K fragment reads and the V transpose reads free of
-//   bank conflicts while every LDS address is one per-lane base plus an
-//   immediate.
-//   Padding slots, rows past the partition end and tiles past the last one are
-//   loaded through buffer resources whose records end there (zeros, no memory
-//   access).
+//   and stalls its wave meanwhile, so every wave issues exactly two loads per
+//   stage, spread over its two phases: its K wave-load at a per-wave step of
+//   its MFMA phase, its V wave-load between the query blocks of its softmax
+//   phase, two tiles ahead of use.  Rows are stored unpadded (a stage is then
+//   16 wave-loads) with the 16-byte chunks of each row permuted by an XOR of
+//   the row index, which keeps the K fragment reads and the V transpose reads
+//   free of bank conflicts; each read address is a per-lane base XOR a per-step
+//   constant plus an immediate.  Rows past the partition end and tiles past
+//   the last one are loaded through buffer resources whose records end there
+//   (zeros, no memory access).
 // * The output accumulator O^T gives each lane one query, so the rescale and
 //   the final 1/l are per-lane scalars.  The first tile takes the exact
 //   running max; later tiles exponentiate against the running max directly and
@@ -64,7 +64,7 @@
 // * Ragged tails: query rows past Nq load a clamped row and are not stored;
 //   key rows past nk read as zero and their scores are set to -inf.
 //
-// Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.12
+// Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.13
 // PFLOP/s, against 1.08 for a four-wave kernel without phase synchronisation.
 
 #include "dita_kernels.h"
@@ -164,6 +164,7 @@ __device__ inline void static_for(F&& f) {
 
 template <int D>
 struct Tile {
+  static constexpr int D_ = D;
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int QB = 2;                       // 32-query blocks per wave
@@ -171,27 +172,41 @@ struct Tile {
   static constexpr int BN = 4096 / D;                // keys per tile: 32 (D=128), 64 (D=64)
   static constexpr int ROW_BYTES = D * 2;            // one K or V row in HBM
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int KS = ROW_BYTES + 16;          // K row stride in LDS
-  static constexpr int VS = ROW_BYTES + 64;          // V row stride in LDS
-  static constexpr int K_SPR = KS / 16;              // 16-byte LDS slots per K row
-  static constexpr int V_SPR = VS / 16;
-  static constexpr int K_REGION = (BN * KS + 1023) / 1024 * 1024;  // whole wave-loads
-  static constexpr int V_REGION = (BN * VS + 1023) / 1024 * 1024;
+  static constexpr int K_REGION = BN * ROW_BYTES;   // 8 KB: whole wave-loads, no padding
+  static constexpr int V_REGION = BN * ROW_BYTES;
   static constexpr int K_WLOADS = K_REGION / 1024;   // wave-wide 16-byte loads per K tile
   static constexpr int V_WLOADS = V_REGION / 1024;
-  static constexpr int WLOADS = K_WLOADS + V_WLOADS;  // per stage, dealt over the 8 waves
+  static constexpr int WLOADS = K_WLOADS + V_WLOADS;  // per stage: two per wave
   static constexpr int TILE_BYTES = BN * ROW_BYTES;  // bytes of one tile in HBM
   static constexpr int STAGE = K_REGION + V_REGION;
   static constexpr int NSTAGE = 5;
-  static_assert(WLOADS <= 24, "a wave's share of a stage is at most three loads");
+  static_assert(K_WLOADS == kWaves && V_WLOADS == kWaves && STAGE % 1024 == 0,
+                "one K and one V wave-load per wave and stage");
 };
 
-// Byte offset, inside a tile in HBM, that fills LDS slot `slot` of a region
-// whose rows are `spr` slots long; padding slots get an offset past any
-// buffer's end, which the buffer load turns into zeros without a memory access.
-__device__ inline uint32_t slot_offset(int slot, int spr, int rows, int cpr, int row_bytes) {
-  const int row = slot / spr, col = slot % spr;
-  return (row < rows && col < cpr) ? uint32_t(row * row_bytes + col * 16) : 0x7ffffff0u;
+// LDS layout of a K or V tile: rows of ROW_BYTES, unpadded, with the 16-byte
+// chunks of each row permuted by an XOR of the row index (physical chunk =
+// logical chunk ^ f(row)).  On gfx950 the LDS serves ds_read_b128 16 lanes at a
+// time and ds_read_b64_tr_b16 32 lanes at a time over 64 four-byte banks; a
+// pattern is conflict-free when the lanes of one pass hit distinct 16-byte
+// (resp. 8-byte) slots modulo 256 bytes (measured: the padded strides that meet
+// this read with zero SQ_LDS_BANK_CONFLICT).  K fragment reads take one chunk
+// from 16 consecutive rows; transpose reads take two adjacent chunks and both
+// 8-byte halves from 4 consecutive rows, for two 32-byte column groups.
+//   D = 128 (16 chunks per row): f_K(r) = r & 15,        f_V(r) = 4 (r & 3)
+//   D = 64  (8 chunks per row):  f_K(r) = (r >> 1) & 7, f_V(r) = 4 ((r >> 1) & 1)
+template <int D>
+__device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// Byte offset, inside a tile in HBM, of the 16 bytes that land in LDS slot
+// `slot` (16-byte units, row-major) of a K (IS_K) or V region.
+template <typename T, bool IS_K>
+__device__ inline uint32_t swz_offset(int slot) {
+  const int row = slot / T::CPR, phys = slot % T::CPR;
+  const int chunk = phys ^ (IS_K ? swz_k<T::D_>(row) : swz_v<T::D_>(row));
+  return uint32_t(row * T::ROW_BYTES + chunk * 16);
 }
 
 // Buffer resource over tile t of one head's K or V: records end at the
@@ -210,56 +225,47 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* head, int t, int 
                                            0x00020000);
 }
 
-// Load J (0, 1, 2) of a wave's share of stage s: the stage's wave-loads
-// (K tile s, then V tile s-1) are dealt round-robin over the eight waves, so
-// wave w issues wave-loads w, w + 8, w + 16.  Stage 0 has no V tile: its V
-// loads use the empty tile past the end, so every wave issues the same number
-// of loads for every stage.  (A plain device function: buffer-resource
-// builtins inside a kernel lambda make the host pass drop the launch stub.)
+// Load J (0 or 1) of a wave's share of stage s: wave w fills K wave-load w
+// (J = 0) and V wave-load w (J = 1) of the stage, K tile s and V tile s-1,
+// with per-lane source offsets fixed for the whole kernel (off_k, off_v).
+// Stage 0 has no V tile: its V loads use the empty tile past the end, so every
+// wave issues the same two loads for every stage.  (A plain device function:
+// buffer-resource builtins inside a kernel lambda make the host pass drop the
+// launch stub.)
 template <typename T, int J>
 __device__ inline void load_share_item(char* smem, int s, int ntiles, const char* k_head,
                                        const char* v_head, uint32_t head_bytes, int wave,
-                                       int lane) {
-  // Opaque copy of the lane index: the offsets are recomputed at every call
-  // instead of being hoisted out of the tile loop into registers it cannot spare.
-  asm volatile("" : "+v"(lane));
+                                       uint32_t off_k, uint32_t off_v) {
   char* base = smem + (s % T::NSTAGE) * T::STAGE;
-  const int k = wave + 8 * J;
-  if (k < T::K_WLOADS) {
+  if constexpr (J == 0) {
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(k_head, s, T::TILE_BYTES, head_bytes);
-    const uint32_t off = slot_offset(k * 64 + lane, T::K_SPR, T::BN, T::CPR, T::ROW_BYTES);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(base + k * 1024), 16, off, 0, 0, 0);
-  } else if (k < T::WLOADS) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(base + wave * 1024), 16, off_k, 0,
+                                             0, 0);
+  } else {
     const __amdgpu_buffer_rsrc_t rv =
         tile_rsrc(v_head, s >= 1 ? s - 1 : ntiles, T::TILE_BYTES, head_bytes);
-    const int i = k - T::K_WLOADS;
-    const uint32_t off = slot_offset(i * 64 + lane, T::V_SPR, T::BN, T::CPR, T::ROW_BYTES);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + T::K_REGION + i * 1024), 16,
-                                             off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + T::K_REGION + wave * 1024),
+                                             16, off_v, 0, 0, 0);
   }
 }
 template <typename T>
 __device__ inline void load_share(char* smem, int s, int ntiles, const char* k_head,
-                                  const char* v_head, uint32_t head_bytes, int wave, int lane) {
-  load_share_item<T, 0>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
-  load_share_item<T, 1>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
-  load_share_item<T, 2>(smem, s, ntiles, k_head, v_head, head_bytes, wave, lane);
+                                  const char* v_head, uint32_t head_bytes, int wave,
+                                  uint32_t off_k, uint32_t off_v) {
+  load_share_item<T, 0>(smem, s, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
+  load_share_item<T, 1>(smem, s, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
 }
 
-// vmcnt waits.  A wave issues n = (WLOADS - wave + 7) / 8 loads per stage; the
-// waits below leave exactly the loads of later stages in flight.
+// vmcnt waits.  Every wave issues two loads per stage; the wait leaves exactly
+// STAGES later stages plus EXTRA single loads in flight.
 template <int N>
 __device__ inline void wait_vm() {
   static_assert(N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
 }
-template <typename T, int STAGES, int EXTRA>
-__device__ inline void wait_stages_in_flight(int wave) {
-  constexpr int LO = T::WLOADS / 8, R = T::WLOADS % 8;
-  if (wave < R)
-    wait_vm<(LO + 1) * STAGES + EXTRA>();
-  else
-    wait_vm<LO * STAGES + EXTRA>();
+template <int STAGES, int EXTRA>
+__device__ inline void wait_stages_in_flight() {
+  wait_vm<2 * STAGES + EXTRA>();
 }
 __device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -300,6 +306,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   const int ntiles = (nk + T::BN - 1) / T::BN;
 
   const uint32_t head_bytes = uint32_t(nk) * T::ROW_BYTES;
+  const uint32_t off_k = swz_offset<T, true>(wave * 64 + lane);
+  const uint32_t off_v = swz_offset<T, false>(wave * 64 + lane);
   const char* k_head = reinterpret_cast<const char*>(job.k) + bh * int64_t(head_bytes);
   const char* v_head = reinterpret_cast<const char*>(job.v) + bh * int64_t(head_bytes);
   const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
@@ -315,12 +323,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 #pragma unroll
   for (int st0 = 0; st0 < 3; ++st0)
-    load_share<T>(smem, st0, ntiles, k_head, v_head, head_bytes, wave, lane);
+    load_share<T>(smem, st0, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
 
-  const int k_lane = m32 * T::KS + 16 * hh;
+  // Per-lane LDS offsets inside a stage; a step adds an immediate and XORs a
+  // constant into bits the lane part leaves clear (the stage base is 1 KB aligned):
+  //   K fragment (block b, k-step kk): (k_lane ^ 32 kk) + 32 b ROW_BYTES
+  //   V transpose read (block b, half h2, read r2, head-dim block d):
+  //     (v_lane ^ 64 d) + (32 b + 16 h2 + 8 r2) ROW_BYTES
+  const int k_lane = m32 * T::ROW_BYTES + 16 * (hh ^ swz_k<D>(m32));
   const int g16 = lane & 15;
   const int gh = (lane >> 4) & 1;
-  const int v_lane = (4 * hh + (g16 >> 2)) * T::VS + 32 * gh + 8 * (g16 & 3);
+  const int vrow = 4 * hh + (g16 >> 2);
+  const int v_lane = vrow * T::ROW_BYTES + 32 * gh + 8 * (g16 & 3) + 16 * swz_v<D>(vrow);
 
   f32x16 oacc[QB][ND];
   float m_run[QB], l_run[QB];
@@ -333,7 +347,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 
   auto compute_s = [&](const char* kreg, f32x16 (*s)[NB]) {
-    const char* kb0 = kreg + k_lane;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -343,7 +356,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(kb0 + b * 32 * T::KS + 32 * kk));
+            as_bf16x8(*reinterpret_cast<const u32x4*>(kreg + (k_lane ^ (32 * kk)) + b * 32 * T::ROW_BYTES));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][kk], s[qb][b], 0, 0, 0);
@@ -394,30 +407,6 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   auto softmax = [&](const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) softmax_qb(qb, s, pb);
-  };
-  auto pv = [&](const char* vreg, bf16x8 (*pb)[NB][2]) {
-    constexpr int G = NB * 2 * ND;
-    const uint32_t va = lds_addr(vreg + v_lane);
-    s16x4 fr[G][2];
-    auto issue = [&](auto gi) {
-      constexpr int g = decltype(gi)::value;
-      constexpr int b = g / (2 * ND), h2 = (g / ND) % 2, d = g % ND;
-      fr[g][0] = tr_read<(32 * b + 16 * h2) * T::VS + 64 * d>(va);
-      fr[g][1] = tr_read<(32 * b + 16 * h2 + 8) * T::VS + 64 * d>(va);
-    };
-    issue(Int<0>{});
-    issue(Int<1>{});
-    static_for<G>([&](auto gi) {
-      constexpr int g = decltype(gi)::value;
-      constexpr int b = g / (2 * ND), h2 = (g / ND) % 2, d = g % ND;
-      lgkm_wait<(g + 1 < G) ? 2 : 0>(fr[g][0], fr[g][1]);
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(fr[g][0], fr[g][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][b][h2], oacc[qb][d], 0, 0, 0);
-      if constexpr (g + 2 < G) issue(Int<g + 2>{});
-    });
   };
   auto rescale_qb = [&](int qb, float mxq) {
     const float m = fmaxf(mxq, __shfl_xor(mxq, 32));
@@ -492,11 +481,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       constexpr int i = decltype(ic)::value;
       if constexpr (i < NPV) {
         constexpr int b = i / (2 * ND), h2 = (i / ND) % 2, d = i % ND;
-        fr[i][0] = tr_read<(32 * b + 16 * h2) * T::VS + 64 * d>(va);
-        fr[i][1] = tr_read<(32 * b + 16 * h2 + 8) * T::VS + 64 * d>(va);
+        uint32_t a = va;
+        asm volatile("" : "+v"(a));  // computed here, not hoisted and kept live
+        a ^= 64 * d;
+        fr[i][0] = tr_read<(32 * b + 16 * h2) * T::ROW_BYTES>(a);
+        fr[i][1] = tr_read<(32 * b + 16 * h2 + 8) * T::ROW_BYTES>(a);
       } else {
         constexpr int j = i - NPV, b = j / NKK, kk = j % NKK;
-        kf[j] = k_read<b * 32 * T::KS + 32 * kk>(ka);
+        uint32_t a = ka;
+        asm volatile("" : "+v"(a));
+        kf[j] = k_read<b * 32 * T::ROW_BYTES>(a ^ (32 * kk));
       }
     };
     static_for<PF>([&](auto c) {
@@ -528,7 +522,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       // differs per wave of the group (staggered use of the address unit).
       if constexpr ((i - FIRST) % 4 == 1 && (i - FIRST) / 4 < 4) {
         if (load_stage_idx >= 0 && wl == (i - FIRST) / 4)
-          load_share_item<T, 0>(smem, load_stage_idx, ntiles, k_head, v_head, head_bytes, wave, lane);
+          load_share_item<T, 0>(smem, load_stage_idx, ntiles, k_head, v_head, head_bytes, wave,
+                                off_k, off_v);
       }
       // Keep the written order: each step's MFMAs before the next step's wait.
       __builtin_amdgcn_sched_barrier(0);
@@ -538,12 +533,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // Phase schedule (group A = waves 0-3, B = waves 4-7):
   //   A: M(0) V(0) M(1) V(1) ... M(T)      B: -- M(0) V(0) ... V(T-1) M(T)
   // M(t) = P V of tile t-1 and S of tile t, reading stage t; V(t) = softmax of
-  // tile t.  Every wave fetches its share of stage t+3 during M(t) (one load,
-  // at a step that differs per wave) and V(t) (the rest), and its share of
-  // stage s has landed by the end of phase 2s-1: group A waits at the end of
+  // tile t.  Every wave fetches its two loads of stage t+3 during M(t) (the K
+  // load, at a step that differs per wave) and V(t) (the V load), and its share
+  // of stage s has landed by the end of phase 2s-1: group A waits at the end of
   // V(s-1) with stages s+1, s+2 still in flight, group B at the end of M(s-1)
-  // with stage s+1 and one load of stage s+2 in flight.
-  wait_stages_in_flight<T, 2, 0>(wave);  // stage 0 (stages 1, 2 in flight)
+  // with stage s+1 and the K load of stage s+2 in flight.
+  wait_stages_in_flight<2, 0>();  // stage 0 (stages 1, 2 in flight)
   phase_barrier();
   if (grp == 1) phase_barrier();
   f32x16 sc[QB][NB];
@@ -551,18 +546,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   if (ntiles > 0) {  // step 0: S only, exact max
     __builtin_amdgcn_s_setprio(1);
     m_phase(Int<NPV>{}, Int<NPV + NS>{}, smem, sc, pb, 3);
-    if (wl >= 2) load_share_item<T, 0>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    if (wl >= 2)
+      load_share_item<T, 0>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_stages_in_flight<T, 1, 1>(wave);
+    if (grp == 1) wait_stages_in_flight<1, 1>();
     phase_barrier();
-    load_share_item<T, 1>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
-    load_share_item<T, 2>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+    load_share_item<T, 1>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
     if (T::BN > nk) mask_tail(0, sc);
     float mx[QB];
     row_max(sc, mx);
     rescale(mx);
     softmax(sc, pb);
-    if (grp == 0) wait_stages_in_flight<T, 2, 0>(wave);
+    if (grp == 0) wait_stages_in_flight<2, 0>();
     phase_barrier();
   }
   for (int t = 1; t < ntiles; ++t) {
@@ -570,20 +565,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     __builtin_amdgcn_s_setprio(1);
     m_phase(Int<0>{}, Int<NPV + NS>{}, st, sc, pb, t + 3);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_stages_in_flight<T, 1, 1>(wave);
+    if (grp == 1) wait_stages_in_flight<1, 1>();
     phase_barrier();
 
     if ((t + 1) * T::BN > nk) mask_tail(t, sc);
     auto loads_between = [&](int qb) {
       __builtin_amdgcn_sched_barrier(0);
       if (qb == (wl & 1))
-        load_share_item<T, 1>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, lane);
+        load_share_item<T, 1>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, off_k,
+                              off_v);
       __builtin_amdgcn_sched_barrier(0);
     };
     const bool fast = softmax_fast(sc, pb, loads_between);
-    __builtin_amdgcn_sched_barrier(0);
-    load_share_item<T, 2>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
     if (!fast) {
       // The fast path consumed the scores: recompute them from the K tile.
       compute_s(smem + (t % T::NSTAGE) * T::STAGE, sc);
@@ -593,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       rescale(mx);
       softmax(sc, pb);
     }
-    if (grp == 0) wait_stages_in_flight<T, 2, 0>(wave);
+    if (grp == 0) wait_stages_in_flight<2, 0>();
     phase_barrier();
   }
   if (ntiles > 0) {
