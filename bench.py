@@ -308,8 +308,8 @@ def trajectory(dita, wl, seed, dev, tdt, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "design is described in DESIGN.md and not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): sharding the "
+              "rank-step across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -6,7 +6,7 @@ An *attention state* of a query block against one K/V context partition is
 the pair (output, log-sum-exp), the composable object of the DiTango page,
 Methodology > 2. State-Centric Parallel Runtime > "State Composition".
 
-Readings taken where the page is silent (each listed in the design doc):
+Readings taken where the page is silent:
 
 * the output of a partial state is normalised by that partition's own
   softmax denominator, so every output row is a convex combination of the

@@ -1,8 +1,8 @@
 """Seeded synthetic Q/K/V for the workloads, shared by the oracle side and the GPU side.
 
 Holds no arithmetic of the method (no scores, softmax, states or merges):
-only the recipe that draws the inputs, described in the design doc, and the
-round-to-nearest-even narrowing that both sides must see identically.
+only the recipe that draws the inputs (below) and the round-to-nearest-even
+narrowing that both sides must see identically.
 
 Recipe
 ------
