@@ -15,9 +15,9 @@
 // * Ping-pong: the waves form two groups of four (A = waves 0-3, B = 4-7; one
 //   wave of each group per SIMD).  Each group alternates an MFMA phase (P V of
 //   tile t-1, then S of tile t) with a softmax phase (exponentials of tile t);
-//   B runs one phase behind A and a workgroup barrier separates phases, so on
-//   every SIMD one wave keeps the matrix core busy while the other issues the
-//   softmax VALU work.  (A lone wave issues a VALU instruction only every ~6-10
+//   B runs one phase behind A and one workgroup barrier per tile re-aligns
+//   them, so on every SIMD one wave keeps the matrix core busy while the other
+//   issues the softmax VALU work.  (A lone wave issues a VALU instruction only every ~6-10
 //   cycles on gfx950, so the softmax of a tile takes about as long as its 32
 //   MFMAs; left unsynchronised, the two waves of a SIMD drift into the same
 //   phase.)
@@ -64,8 +64,9 @@
 // * Ragged tails: query rows past Nq load a clamped row and are not stored;
 //   key rows past nk read as zero and their scores are set to -inf.
 //
-// Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.13
-// PFLOP/s, against 1.08 for a four-wave kernel without phase synchronisation.
+// Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.15
+// PFLOP/s, against 1.08 for a four-wave kernel without phase synchronisation
+// and 1.11 with a barrier between every two phases.
 
 #include "dita_kernels.h"
 
@@ -530,17 +531,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     });
   };
 
-  // Phase schedule (group A = waves 0-3, B = waves 4-7):
-  //   A: M(0) V(0) M(1) V(1) ... M(T)      B: -- M(0) V(0) ... V(T-1) M(T)
+  // Phase schedule (group A = waves 0-3, B = waves 4-7), one barrier per tile:
+  //   A: M(t) V(t) | M(t+1) V(t+1) | ...      B: M(t) | V(t) M(t+1) | ...
   // M(t) = P V of tile t-1 and S of tile t, reading stage t; V(t) = softmax of
-  // tile t.  Every wave fetches its two loads of stage t+3 during M(t) (the K
-  // load, at a step that differs per wave) and V(t) (the V load), and its share
-  // of stage s has landed by the end of phase 2s-1: group A waits at the end of
-  // V(s-1) with stages s+1, s+2 still in flight, group B at the end of M(s-1)
-  // with stage s+1 and the K load of stage s+2 in flight.
+  // tile t.  The barrier after A's V(t) and B's M(t) re-aligns the groups every
+  // tile, so A's MFMA phase runs beside B's softmax phase and the other way
+  // round (B starts one phase late: its first M overlaps A's first two).
+  // Every wave fetches its two loads of stage t+3 during M(t) (the K load, at a
+  // step that differs per wave) and V(t) (the V load); its share of stage s has
+  // landed at the barrier that ends tile s-1: group A waits at the end of
+  // V(s-1) with stages s+1, s+2 in flight, group B at the end of M(s-1) with
+  // stage s+1 and the K load of stage s+2 in flight.  Stage t is rewritten by
+  // stage t+5, whose first load A issues after the barrier that ends tile t+1,
+  // when B's softmax of tile t (whose exact path may re-read K tile t) is done.
   wait_stages_in_flight<2, 0>();  // stage 0 (stages 1, 2 in flight)
   phase_barrier();
-  if (grp == 1) phase_barrier();
   f32x16 sc[QB][NB];
   bf16x8 pb[QB][NB][2];
   if (ntiles > 0) {  // step 0: S only, exact max
@@ -549,24 +554,30 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     if (wl >= 2)
       load_share_item<T, 0>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_stages_in_flight<1, 1>();
-    phase_barrier();
+    if (grp == 1) {
+      wait_stages_in_flight<1, 1>();
+      phase_barrier();
+    }
     load_share_item<T, 1>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
     if (T::BN > nk) mask_tail(0, sc);
     float mx[QB];
     row_max(sc, mx);
     rescale(mx);
     softmax(sc, pb);
-    if (grp == 0) wait_stages_in_flight<2, 0>();
-    phase_barrier();
+    if (grp == 0) {
+      wait_stages_in_flight<2, 0>();
+      phase_barrier();
+    }
   }
   for (int t = 1; t < ntiles; ++t) {
     const char* st = smem + (t % T::NSTAGE) * T::STAGE;
     __builtin_amdgcn_s_setprio(1);
     m_phase(Int<0>{}, Int<NPV + NS>{}, st, sc, pb, t + 3);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) wait_stages_in_flight<1, 1>();
-    phase_barrier();
+    if (grp == 1) {
+      wait_stages_in_flight<1, 1>();
+      phase_barrier();
+    }
 
     if ((t + 1) * T::BN > nk) mask_tail(t, sc);
     auto loads_between = [&](int qb) {
@@ -586,15 +597,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       rescale(mx);
       softmax(sc, pb);
     }
-    if (grp == 0) wait_stages_in_flight<2, 0>();
-    phase_barrier();
+    if (grp == 0) {
+      wait_stages_in_flight<2, 0>();
+      phase_barrier();
+    }
   }
   if (ntiles > 0) {
     __builtin_amdgcn_s_setprio(1);
     m_phase(Int<0>{}, Int<NPV>{}, smem + (ntiles % T::NSTAGE) * T::STAGE, sc, pb, -1);
     __builtin_amdgcn_s_setprio(0);
   }
-  if (grp == 0) phase_barrier();
   wait_loads();  // the zero-filling loads past the last stage must land before LDS is released
 
 #pragma unroll
