@@ -15,12 +15,14 @@ paper 2607.15650), section "Methodology":
   local partition, the compute-or-reuse decision per partition), and
 * "2. State-Centric Parallel Runtime" -> "State Composition" (an attention
   state is an output plus its log-sum-exp; states compose associatively and
-  commutatively; composed states are cached instead of raw K/V).
+  commutatively; composed states are cached instead of raw K/V) and "Dynamic
+  Group Compose" (cached states merged recursively into coarser groups).
 
 Modules
 -------
 attention  partial attention state, LSE merge, full attention (float64).
-cache      the per-partition state cache and one compute-or-reuse rank-step.
+cache      the per-partition state cache, group composition and one
+           compute-or-reuse rank-step.
 planner    the reuse-mask planner and its SplitMix64 integer generator.
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
@@ -32,7 +34,7 @@ which the pages give no numbers for.
 """
 
 from .attention import full_attention, merge_states, partial_state, softmax_scale
-from .cache import StateCache, attn_step
+from .cache import StateCache, attn_step, effective_reuse
 from .planner import (
     POLICY_DIST,
     POLICY_KNEAREST,
@@ -51,6 +53,7 @@ __all__ = [
     "full_attention",
     "StateCache",
     "attn_step",
+    "effective_reuse",
     "Plan",
     "SplitMix64",
     "plan_mask",

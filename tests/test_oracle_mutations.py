@@ -26,7 +26,7 @@ import pytest
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 PINS = {
     "attention.py": ["test_oracle_attention", "test_oracle_merge"],
-    "cache.py": ["test_oracle_merge"],
+    "cache.py": ["test_oracle_merge", "test_oracle_groups"],
     "planner.py": ["test_oracle_planner", "test_abi"],
 }
 
@@ -65,8 +65,18 @@ MUTATIONS = [
      "partial_state(q, k_parts[p], v_parts[0], scale)"),
     ("cache.py", "stamp not recorded", "self.stamp[p] = step", "self.stamp[p] = 0"),
     ("cache.py", "merge over the fresh slots only",
-     "o, lse = merge_states(cache.slots)",
-     "o, lse = merge_states([s for s, r in zip(cache.slots, reuse) if not r] or cache.slots)"),
+     "o, lse = merge_states([cache.slots[p] for p in cache.leaders()])",
+     "o, lse = merge_states([cache.slots[p] for p in cache.leaders() if not reuse[p]] or [cache.slots[0]])"),
+    ("cache.py", "group composed from its first state only",
+     "state = merge_states([self.slots[p] for p in heads])",
+     "state = merge_states([self.slots[p] for p in heads[:1]])"),
+    ("cache.py", "group stamp from the newest member",
+     "oldest = min(int(self.stamp[p]) for p in heads)", "oldest = max(int(self.stamp[p]) for p in heads)"),
+    ("cache.py", "group reused when any member is reused",
+     "if last > first and not reuse[first:last + 1].all():",
+     "if last > first and not reuse[first:last + 1].any():"),
+    ("cache.py", "group range one short", "while last + 1 < self.P and self.group[last + 1] == first:",
+     "while last + 2 < self.P and self.group[last + 1] == first:"),
     ("cache.py", "reuse of an empty slot not rejected",
      "if reuse[p] and not cache.valid[p]:", "if False:"),
     ("planner.py", "SplitMix64 multiplier typo", "0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
@@ -153,7 +163,7 @@ def test_unmodified_copy_passes_every_pin(tmp_path):
     modules = sorted({m for ms in PINS.values() for m in ms})
     failed, n_run = _run_pins(tmp_path, modules)
     assert failed == []
-    assert n_run >= 60, n_run   # every parametrised pin case ran
+    assert n_run >= 70, n_run   # every parametrised pin case ran
 
 
 @pytest.mark.parametrize("fname,what,old,new", MUTATIONS, ids=[m[1] for m in MUTATIONS])
