@@ -17,6 +17,12 @@ roofline of the dominant kernel (the fresh-attention launch, timed with HIP
 events on its own stream), the merge's bandwidth, and the fp64 CPU oracle
 timed on a bounded sample of the same step.
 
+By default (--compose-ahead 1) each step is followed, inside the timed
+region, by the composition of the partitions the next step will reuse into
+groups (Dynamic Group Compose), so a step's merge reads one state per group;
+--premerge 1 instead (or also) merges the reused states on a second stream
+while the fresh attention runs.
+
 With --trajectory the schedule also runs once from a cold cache beside an
 all-fresh reference computed by the same library on the same K/V (every
 partition recomputed, which equals full attention): per step the fresh
@@ -67,6 +73,12 @@ def parse():
     ap.add_argument("--resident-steps", type=int, default=0,
                     help="distinct K/V steps to generate (0: the whole schedule); step s uses "
                          "inputs s mod this, for short profiling runs")
+    ap.add_argument("--premerge", type=int, default=0, choices=(0, 1),
+                    help="1: merge the reused states on a second stream while the fresh "
+                         "attention runs (dita_attn_step_ex)")
+    ap.add_argument("--compose-ahead", type=int, default=1, choices=(0, 1),
+                    help="1: after each step compose the runs of partitions the next step "
+                         "reuses into groups (dita_state_cache_compose_runs); timed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the library's state-copy kernel over BYTES of O (the "
                          "reference point for HBM byte counters) and exit")
@@ -246,7 +258,7 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
     }
 
 
-def trajectory(dita, wl, seed, dev, tdt, stream):
+def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False):
     """The schedule once from a cold cache beside an all-fresh reference (same library,
     same K/V, every partition recomputed): per-step error of the reused output, fresh
     blocks, step latency, and the contribution profile by partition distance."""
@@ -273,6 +285,8 @@ def trajectory(dita, wl, seed, dev, tdt, stream):
         ev = (dita.Event(), dita.Event(), dita.Event())
         _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, s, o=o, lse=lse, stream=stream,
                                          events=(ev[0].handle, ev[1].handle, ev[2].handle))
+        if compose_ahead and s + 1 < wl.steps:
+            cache.compose_runs(dita.dita_plan_mask(plan, s + 1, cache), stream=stream)
         dita.dita_attn_step(ref, q, ks, vs, all_fresh, s, o=o_ref, lse=lse_ref, stream=stream)
         torch.cuda.synchronize()
         d = o.float() - o_ref.float()
@@ -343,12 +357,21 @@ def main():
     lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    side = torch.cuda.Stream(device=dev) if args.premerge else None
+
     def run(step_index, events=None):
         si = step_index % n_sched
         mask = dita.dita_plan_mask(plan, si, cache)
         ks, vs = kv[si % n_res]
         _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, step_index, o=o, lse=lse,
-                                         stream=stream, events=events)
+                                         stream=stream, events=events and events[:3],
+                                         side_stream=side)
+        if args.compose_ahead:
+            # the planner is deterministic: compose what the next step will reuse
+            nxt = dita.dita_plan_mask(plan, (step_index + 1) % n_sched, cache)
+            cache.compose_runs(nxt, stream=stream)
+        if events:
+            assert dita.lib().dita_event_record(events[3], stream.cuda_stream) == 0
         return info
 
     for s in range(args.warmup):
@@ -357,7 +380,7 @@ def main():
     log(f"[bench] warmup done ({args.warmup} steps)")
 
     K = args.steps
-    evs = [(dita.Event(), dita.Event(), dita.Event()) for _ in range(K)]
+    evs = [(dita.Event(), dita.Event(), dita.Event(), dita.Event()) for _ in range(K)]
     t_begin, t_end = dita.Event(), dita.Event()
     infos = []
     torch.cuda.synchronize()
@@ -365,14 +388,15 @@ def main():
     t_begin.record(stream)
     for i in range(K):
         e = evs[i]
-        infos.append(run(args.warmup + i, events=(e[0].handle, e[1].handle, e[2].handle)))
+        infos.append(run(args.warmup + i, events=tuple(x.handle for x in e)))
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_begin.elapsed_ms(t_end)
     attn_ms = [e[0].elapsed_ms(e[1]) for e in evs]
     merge_ms = [e[1].elapsed_ms(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_ms(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_ms(e[3]) for e in evs]
+    compose_ms = [e[2].elapsed_ms(e[3]) for e in evs]
     fresh_flops = sum(i.fresh_flops for i in infos)
     fresh_blocks = sum(i.n_fresh for i in infos)
     merge_bytes = sum(i.merge_bytes for i in infos)
@@ -382,6 +406,8 @@ def main():
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     merge_gbs = merge_bytes / (sum(merge_ms) / 1e3) / 1e9
     traffic_attn, traffic_merge = profiled_traffic(wl.name)
+    if args.premerge or args.compose_ahead:
+        traffic_merge = None   # the counters were taken on the P-way merge of the plain step
     log(f"[bench] timed {K} steps: {total_ms:.3f} ms (host wall {wall * 1e3:.1f} ms); "
         f"attention {sum(attn_ms):.3f} ms, merge {sum(merge_ms):.3f} ms")
 
@@ -406,12 +432,19 @@ def main():
                      "radius": wl.radius, "radius_end": wl.radius_end, "k_nearest": wl.k_nearest,
                      "anchor_period": wl.anchor_period},
             "parallelism": "one rank's share on one GPU",
+            "pipeline": {"premerge_side_stream": bool(args.premerge),
+                         "compose_ahead": bool(args.compose_ahead)},
         },
         "fresh_blocks": fresh_blocks,
         "fresh_fraction": fresh_blocks / (K * wl.P),
         "fresh_tflop": fresh_flops / 1e12,
         "attn_ms_per_step": sum(attn_ms) / K,
         "merge_ms_per_step": sum(merge_ms) / K,
+        "compose_ms_per_step": sum(compose_ms) / K,
+        "premerge": bool(args.premerge),
+        "compose_ahead": bool(args.compose_ahead),
+        "merge_sources_per_step": [i.merge_sources for i in infos],
+        "premerge_sources_per_step": [i.premerge_sources for i in infos],
         "step_ms": [round(x, 4) for x in step_ms],
         "step_ms_median": float(np.median(step_ms)),
         "step_ms_min": float(np.min(step_ms)),
@@ -442,7 +475,8 @@ def main():
         del kv, cache
         torch.cuda.empty_cache()
         log("[bench] trajectory: the schedule from a cold cache beside an all-fresh reference")
-        result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream)
+        result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream,
+                                          compose_ahead=bool(args.compose_ahead))
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)

@@ -130,7 +130,21 @@ int dita_state_merge(const dita_shape* shape, int P, const void* const* o_list,
  * memory (16-byte aligned; 256 recommended) and keeps it alive while the
  * handle exists.  Slot p holds O_p ([B, H, Nq, D] dtype) followed by LSE_p
  * ([B, H, Nq] float32), each at a 256-byte aligned offset.  Host metadata per
- * slot: valid (0/1) and stamp (the step that last wrote it, -1 if never).
+ * slot: valid (0/1), stamp (the step that last wrote it, -1 if never) and the
+ * group the partition belongs to.
+ *
+ * Groups (page section: State-Centric Parallel Runtime > Dynamic Group
+ * Compose -- cached states are merged recursively into coarser groups).  A
+ * group is a contiguous range [first, last] of partitions whose states have
+ * been composed into one state held in slot `first` (the leader); the other
+ * member slots hold nothing of their own.  Every partition starts as a group
+ * of one.  A group's stamp is the oldest stamp among the states composed into
+ * it and is reported for every member.  Rules: a group is reused by a step
+ * only when every member is marked reuse, otherwise every member is computed
+ * fresh and the group dissolves into groups of one; store into any partition
+ * of a group of two or more, and load from a member other than the leader,
+ * return DITA_ERR_STATE; invalidating any member invalidates and dissolves
+ * the whole group.
  */
 typedef struct dita_state_cache dita_state_cache;
 
@@ -147,14 +161,17 @@ int dita_state_cache_free(dita_state_cache* cache);
 /* Device addresses of slot p's O and LSE (either output pointer may be NULL). */
 int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse);
 
-/* Copy a state into slot p (stream-ordered copy kernel) and mark it valid with `step`. */
+/* Copy a state into slot p (stream-ordered copy kernel) and mark it valid with `step`.
+ * DITA_ERR_STATE if p belongs to a group of two or more partitions. */
 int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const float* lse,
                            int64_t step, void* stream);
 
-/* Copy slot p out to caller buffers.  DITA_ERR_STATE if the slot is invalid. */
+/* Copy slot p out to caller buffers (for a group leader: the group's state).
+ * DITA_ERR_STATE if the slot is invalid or p is a group member other than the leader. */
 int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* lse, void* stream);
 
-/* Mark slot p invalid (p = -1: every slot).  Device memory is untouched. */
+/* Mark slot p invalid, with every other member of its group (p = -1: every
+ * slot); the group dissolves.  Device memory is untouched. */
 int dita_state_cache_invalidate(dita_state_cache* cache, int p);
 
 /* Read slot p's metadata (either output pointer may be NULL). */
@@ -162,6 +179,47 @@ int dita_state_cache_info(const dita_state_cache* cache, int p, int* valid, int6
 
 /* Cache geometry: P, and the shape it was created with. */
 int dita_state_cache_shape(const dita_state_cache* cache, dita_shape* shape, int* P);
+
+/*
+ * Compose the cached states of partitions first..last into one group state,
+ * written in place into slot `first` by the LSE merge kernel (groups already
+ * inside the range enter as the single states they are, so composition is
+ * recursive).  Page section: State-Centric Parallel Runtime > Dynamic Group
+ * Compose.  Reads the range's leader slots and writes one state: with n
+ * leaders, (n + 1) * (B*H*Nq*(D*size + 4)) bytes; no launch when the range
+ * already is one group.
+ * Errors: DITA_ERR_ARG unless 0 <= first <= last < P, or when a group
+ * straddles the range; DITA_ERR_STATE when a partition in it holds no state.
+ */
+int dita_state_cache_compose(dita_state_cache* cache, int first, int last, void* stream);
+
+/*
+ * Compose ahead of a step: for every maximal run of partitions that `reuse`
+ * (P bytes, 0/1 -- typically the next step's mask) marks for reuse, compose
+ * the run into one group, leaving out groups that reach outside the run (a
+ * step recomputes those whole).  Runs that already are one group, or hold one
+ * partition, are left as they are.  A step with that mask then reads one state
+ * per run.  *n_launched (nullable) receives the number of merge launches.
+ * DITA_ERR_STATE if `reuse` marks an invalid slot; DITA_ERR_ARG for values
+ * other than 0/1.
+ */
+int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse, void* stream,
+                                  int* n_launched);
+
+/* The group [*first, *last] that holds partition p (either output may be NULL). */
+int dita_state_cache_group(const dita_state_cache* cache, int p, int* first, int* last);
+
+/* Number of states the cache holds: valid group leaders (a lone partition leads its own group). */
+int dita_state_cache_live(const dita_state_cache* cache, int* live);
+
+/*
+ * The reuse mask a step applies for the caller's mask `reuse` (P bytes, 0/1):
+ * equal to `reuse` except that a group with any member marked fresh is
+ * computed fresh whole.  The caller must supply K/V for every partition whose
+ * entry in `out` is 0.  DITA_ERR_STATE if `reuse` marks an invalid slot.
+ */
+int dita_state_cache_effective_mask(const dita_state_cache* cache, const uint8_t* reuse,
+                                    uint8_t* out);
 
 /*
  * Reuse-mask planner (host only, integer arithmetic, deterministic).
@@ -207,13 +265,15 @@ int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t
  * For every p with reuse_mask[p] == 0 the fresh state of Q against
  * (k_list[p], v_list[p]) is written straight into cache slot p (one grouped
  * launch for all fresh partitions) and the slot is stamped with `step`; slots
- * with reuse_mask[p] == 1 are left as they are and must be valid.  Then all P
- * slots are merged into (o, lse).  Shape and P come from the cache.
+ * with reuse_mask[p] == 1 are left as they are and must be valid.  Composed
+ * groups are reused or recomputed whole (see the cache's group rules and
+ * dita_state_cache_effective_mask).  Then the states of all groups are merged
+ * into (o, lse).  Shape and P come from the cache.
  *
  * q                [in]  device [B, H, Nq, D]
  * k_list, v_list   [in]  host arrays of P device pointers, [B, H, nk_list[p], D];
  *                        entries of reused partitions are not read (may be NULL)
- * nk_list          [in]  host array of P key counts (>= 1 where fresh)
+ * nk_list          [in]  host array of P key counts (>= 1 where computed)
  * reuse_mask       [in]  host array of P bytes (0 fresh, 1 reuse; other values rejected)
  * o, lse           [out] device final output and LSE
  * info             [in/out, nullable] step report; its `events` members, when
@@ -221,18 +281,50 @@ int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t
  *                  step start, after the fresh-attention launch and at the end.
  */
 typedef struct {
-  int32_t n_fresh;       /* [out] partitions computed fresh             */
-  int32_t n_reused;      /* [out] partitions reused                     */
-  double fresh_flops;    /* [out] 4*B*H*Nq*sum(nk of fresh)*D           */
-  double merge_bytes;    /* [out] (P+1) * bytes of one state            */
-  void* ev_begin;        /* [in] hipEvent_t or NULL                     */
-  void* ev_attn_end;     /* [in] hipEvent_t or NULL                     */
-  void* ev_end;          /* [in] hipEvent_t or NULL                     */
+  int32_t n_fresh;          /* [out] partitions computed fresh                          */
+  int32_t n_reused;         /* [out] partitions reused                                  */
+  double fresh_flops;       /* [out] 4*B*H*Nq*sum(nk of fresh)*D                        */
+  double merge_bytes;       /* [out] (merge_sources + 1) * bytes of one state           */
+  void* ev_begin;           /* [in] hipEvent_t or NULL                                  */
+  void* ev_attn_end;        /* [in] hipEvent_t or NULL                                  */
+  void* ev_end;             /* [in] hipEvent_t or NULL                                  */
+  int32_t merge_sources;    /* [out] states read by the final merge on `stream`         */
+  int32_t premerge_sources; /* [out] reused states pre-merged on the side stream, or 0  */
+  double premerge_bytes;    /* [out] (premerge_sources + 1) * bytes of one state, or 0  */
 } dita_step_info;
 
 int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
                    const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
                    int64_t step, void* o, float* lse, void* stream, dita_step_info* info);
+
+/*
+ * dita_attn_step_ex -- dita_attn_step with the reused states composed off the
+ * critical path.  Page section: State-Centric Parallel Runtime > Pipeline
+ * Orchestration (reuse operations fill the bubbles of the compute pipeline).
+ *
+ * When opts->side_stream is non-NULL and differs from `stream`, at least one
+ * partition is fresh and at least max(2, opts->min_premerge) group states are
+ * reused, the reused states are merged into (o, lse) on the side stream while
+ * the fresh attention runs on `stream`; the final merge on `stream` then reads
+ * (o, lse) and the fresh states only and writes (o, lse) in place.  The two
+ * streams are ordered by events the handle owns (created on first use, with
+ * timing disabled, destroyed by dita_state_cache_free): the side stream waits
+ * for all work enqueued on `stream` before the step, and `stream` waits for
+ * the pre-merge before its final merge, so on return every effect is ordered
+ * on `stream` as in dita_attn_step.  The result equals dita_attn_step's up to
+ * the order of the fp32 sums.  opts == NULL, or no pre-merge taken, is exactly
+ * dita_attn_step.
+ */
+typedef struct {
+  void* side_stream;     /* hipStream_t for the pre-merge, or NULL                  */
+  int32_t min_premerge;  /* pre-merge only with at least this many reused states   */
+  int32_t reserved;      /* must be 0                                              */
+} dita_step_opts;
+
+int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const* k_list,
+                      const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
+                      int64_t step, void* o, float* lse, void* stream, const dita_step_opts* opts,
+                      dita_step_info* info);
 
 /*
  * Timing helpers (thin wrappers over HIP events, for benchmarks that time the

@@ -34,7 +34,7 @@ which the pages give no numbers for.
 """
 
 from .attention import full_attention, merge_states, partial_state, softmax_scale
-from .cache import StateCache, attn_step, effective_reuse
+from .cache import StateCache, attn_step, compose_runs, effective_reuse
 from .planner import (
     POLICY_DIST,
     POLICY_KNEAREST,
@@ -54,6 +54,7 @@ __all__ = [
     "StateCache",
     "attn_step",
     "effective_reuse",
+    "compose_runs",
     "Plan",
     "SplitMix64",
     "plan_mask",

@@ -21,7 +21,7 @@ slots of the range hold nothing of their own any more.  Reading taken where the
 page is silent: a group is reused only as a whole -- when every member is
 marked reuse -- and otherwise all of its members are recomputed fresh, which
 dissolves it back into single-partition slots.  A group's stamp is the oldest
-stamp among the states composed into it.
+stamp among the states composed into it, and every member carries it.
 """
 
 from __future__ import annotations
@@ -117,8 +117,48 @@ class StateCache:
             self.slots[p] = None
             self.group[p] = first
             self.valid[p] = 1
+            self.stamp[p] = oldest
         self.slots[first] = (state[0], state[1])
-        self.stamp[first] = oldest
+
+
+def compose_runs(cache: StateCache, reuse: Sequence[int]) -> int:
+    """Compose ahead of a step: each maximal run of partitions that ``reuse``
+    marks for reuse becomes one group, without the groups that reach outside
+    the run (a step with this mask recomputes those whole).  A run of one
+    partition, or one that already is a single group, is left alone.
+    Returns the number of compositions that merged two or more states.
+
+    Reading taken where the page is silent: the page composes cached states
+    into coarser groups but names no rule for which; composing exactly what
+    the next step reuses keeps every group reusable whole at that step."""
+    reuse = np.asarray(reuse, dtype=np.uint8)
+    for p in range(cache.P):
+        if reuse[p] and not cache.valid[p]:
+            raise RuntimeError(f"partition {p} is marked reuse but its slot is empty")
+    runs = []
+    p = 0
+    while p < cache.P:
+        if not reuse[p]:
+            p += 1
+            continue
+        a = p
+        while p + 1 < cache.P and reuse[p + 1]:
+            p += 1
+        b = p
+        p += 1
+        inside = [i for i in range(a, b + 1)
+                  if cache.group_range(i)[0] >= a and cache.group_range(i)[1] <= b]
+        if not inside:
+            continue
+        lo, hi = min(inside), max(inside)
+        if lo < hi and cache.group_range(lo) != (lo, hi):
+            runs.append((lo, hi))
+    merged = 0
+    for a, b in runs:
+        heads = [i for i in range(a, b + 1) if cache.group[i] == i]
+        merged += len(heads) > 1
+        cache.compose(a, b)
+    return merged
 
 
 def effective_reuse(cache: StateCache, reuse: Sequence[int]) -> np.ndarray:

@@ -14,6 +14,7 @@ The functions carry the names of the C entry points declared in
     dita_state_cache_*  device-resident per-partition state store (``StateCache`` wraps them)
     dita_plan_mask      host reuse-mask planner
     dita_attn_step      one compute-or-reuse rank-step over all P partitions
+    dita_attn_step_ex   the same, with reused states pre-merged on a side stream
 """
 
 from __future__ import annotations
@@ -59,7 +60,13 @@ class StepInfo(ctypes.Structure):
     _fields_ = [("n_fresh", ctypes.c_int32), ("n_reused", ctypes.c_int32),
                 ("fresh_flops", ctypes.c_double), ("merge_bytes", ctypes.c_double),
                 ("ev_begin", ctypes.c_void_p), ("ev_attn_end", ctypes.c_void_p),
-                ("ev_end", ctypes.c_void_p)]
+                ("ev_end", ctypes.c_void_p), ("merge_sources", ctypes.c_int32),
+                ("premerge_sources", ctypes.c_int32), ("premerge_bytes", ctypes.c_double)]
+
+
+class StepOpts(ctypes.Structure):
+    _fields_ = [("side_stream", ctypes.c_void_p), ("min_premerge", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -89,8 +96,19 @@ def _load() -> ctypes.CDLL:
         "dita_state_cache_info": (i32, [vp, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(i64)]),
         "dita_state_cache_shape": (i32, [vp, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int)]),
         "dita_plan_mask": (i32, [ctypes.POINTER(Plan), vp, i64, ctypes.POINTER(ctypes.c_uint8)]),
+        "dita_state_cache_compose": (i32, [vp, i32, i32, vp]),
+        "dita_state_cache_compose_runs": (i32, [vp, ctypes.POINTER(ctypes.c_uint8), vp,
+                                                ctypes.POINTER(ctypes.c_int)]),
+        "dita_state_cache_group": (i32, [vp, i32, ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_int)]),
+        "dita_state_cache_live": (i32, [vp, ctypes.POINTER(ctypes.c_int)]),
+        "dita_state_cache_effective_mask": (i32, [vp, ctypes.POINTER(ctypes.c_uint8),
+                                                  ctypes.POINTER(ctypes.c_uint8)]),
         "dita_attn_step": (i32, [vp, vp, pvp, pvp, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_uint8),
                                  i64, vp, vp, vp, ctypes.POINTER(StepInfo)]),
+        "dita_attn_step_ex": (i32, [vp, vp, pvp, pvp, ctypes.POINTER(i64),
+                                    ctypes.POINTER(ctypes.c_uint8), i64, vp, vp, vp,
+                                    ctypes.POINTER(StepOpts), ctypes.POINTER(StepInfo)]),
         "dita_event_create": (i32, [pvp]),
         "dita_event_destroy": (i32, [vp]),
         "dita_event_record": (i32, [vp, vp]),
@@ -288,6 +306,49 @@ class StateCache:
     def valid_mask(self) -> np.ndarray:
         return np.array([self.info(p)[0] for p in range(self.P)], dtype=np.uint8)
 
+    def compose(self, first: int, last: int, stream=None):
+        """Merge the states of partitions first..last into one group state in slot ``first``."""
+        st = _stream(self.buffer, stream)
+        _check(_lib.dita_state_cache_compose(self.handle, first, last, st), "dita_state_cache_compose")
+
+    def compose_runs(self, reuse_mask, stream=None) -> int:
+        """Compose every run of partitions ``reuse_mask`` marks for reuse; returns the
+        number of merge launches."""
+        mask = np.ascontiguousarray(np.asarray(reuse_mask, dtype=np.uint8))
+        if mask.shape != (self.P,):
+            raise ValueError("reuse mask must have P entries")
+        m = (ctypes.c_uint8 * self.P).from_buffer_copy(mask.tobytes())
+        n = ctypes.c_int()
+        _check(_lib.dita_state_cache_compose_runs(self.handle, m, _stream(self.buffer, stream),
+                                                  ctypes.byref(n)), "dita_state_cache_compose_runs")
+        return n.value
+
+    def group(self, p: int):
+        """(first, last) of the group holding partition p."""
+        a, b = ctypes.c_int(), ctypes.c_int()
+        _check(_lib.dita_state_cache_group(self.handle, p, ctypes.byref(a), ctypes.byref(b)),
+               "dita_state_cache_group")
+        return a.value, b.value
+
+    def leaders(self) -> List[int]:
+        return [p for p in range(self.P) if self.group(p)[0] == p]
+
+    def live(self) -> int:
+        n = ctypes.c_int()
+        _check(_lib.dita_state_cache_live(self.handle, ctypes.byref(n)), "dita_state_cache_live")
+        return n.value
+
+    def effective_mask(self, reuse_mask) -> np.ndarray:
+        """The mask a step applies for ``reuse_mask`` (groups are reused or recomputed whole)."""
+        mask = np.ascontiguousarray(np.asarray(reuse_mask, dtype=np.uint8))
+        if mask.shape != (self.P,):
+            raise ValueError("reuse mask must have P entries")
+        m = (ctypes.c_uint8 * self.P).from_buffer_copy(mask.tobytes())
+        out = (ctypes.c_uint8 * self.P)()
+        _check(_lib.dita_state_cache_effective_mask(self.handle, m, out),
+               "dita_state_cache_effective_mask")
+        return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
     def close(self):
         if self.handle:
             _lib.dita_state_cache_free(self.handle)
@@ -301,12 +362,14 @@ class StateCache:
 
 
 def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reuse_mask,
-                   step: int, o=None, lse=None, stream=None, events=None) -> StepInfo:
-    """One rank-step: fresh states into their slots, reused slots kept, all P merged.
+                   step: int, o=None, lse=None, stream=None, events=None, side_stream=None,
+                   min_premerge: int = 0) -> StepInfo:
+    """One rank-step: fresh states into their slots, reused slots kept, all groups merged.
 
     ``k_list``/``v_list`` hold P tensors [B,H,Nk_p,D] (entries of reused partitions may
     be None).  ``events``: optional (begin, attn_end, end) raw hipEvent_t handles.
-    Returns (o, lse, StepInfo).
+    ``side_stream`` (a torch stream) selects ``dita_attn_step_ex``: reused states are
+    pre-merged there while the fresh attention runs.  Returns (o, lse, StepInfo).
     """
     torch = _torch()
     P = cache.P
@@ -325,9 +388,15 @@ def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reu
     if events is not None:
         info.ev_begin, info.ev_attn_end, info.ev_end = events
     m = (ctypes.c_uint8 * P).from_buffer_copy(mask.tobytes())
-    _check(_lib.dita_attn_step(cache.handle, _ptr(q), _ptr_array([_ptr(k) for k in k_list]),
-                               _ptr_array([_ptr(v) for v in v_list]), nk, m, step, _ptr(o),
-                               _ptr(lse), _stream(q, stream), ctypes.byref(info)), "dita_attn_step")
+    args = (cache.handle, _ptr(q), _ptr_array([_ptr(k) for k in k_list]),
+            _ptr_array([_ptr(v) for v in v_list]), nk, m, step, _ptr(o), _ptr(lse),
+            _stream(q, stream))
+    if side_stream is None:
+        _check(_lib.dita_attn_step(*args, ctypes.byref(info)), "dita_attn_step")
+    else:
+        opts = StepOpts(side_stream.cuda_stream, int(min_premerge), 0)
+        _check(_lib.dita_attn_step_ex(*args, ctypes.byref(opts), ctypes.byref(info)),
+               "dita_attn_step_ex")
     return o, lse, info
 
 

@@ -25,6 +25,9 @@ struct dita_state_cache {
   size_t slot_stride;  // bytes per slot
   uint8_t valid[DITA_MAX_PARTITIONS];
   int64_t stamp[DITA_MAX_PARTITIONS];
+  int16_t group[DITA_MAX_PARTITIONS];  // leader (first partition) of p's group
+  hipEvent_t ev_fork;                  // stream -> side stream, created on first use
+  hipEvent_t ev_join;                  // side stream -> stream
 };
 
 namespace {
@@ -105,6 +108,78 @@ float* slot_lse(const dita_state_cache* c, int p) {
   return reinterpret_cast<float*>(c->base + size_t(p) * c->slot_stride + c->lse_offset);
 }
 
+// Last partition of the group led by `first`.
+int group_last(const dita_state_cache* c, int first) {
+  int last = first;
+  while (last + 1 < c->P && c->group[last + 1] == first) ++last;
+  return last;
+}
+
+void reset_slot(dita_state_cache* c, int p) {
+  c->valid[p] = 0;
+  c->stamp[p] = -1;
+  c->group[p] = int16_t(p);
+}
+
+// The mask a step applies: a group of two or more is reused only when every
+// member is marked reuse.  Returns DITA_ERR_ARG for mask values other than
+// 0/1 and DITA_ERR_STATE for reuse of an invalid slot.
+int effective_mask(const dita_state_cache* c, const uint8_t* reuse, uint8_t* out) {
+  for (int p = 0; p < c->P; ++p) {
+    if (reuse[p] > 1) return DITA_ERR_ARG;
+    if (reuse[p] && !c->valid[p]) return DITA_ERR_STATE;
+  }
+  for (int p = 0; p < c->P;) {
+    const int last = group_last(c, p);
+    uint8_t all = 1;
+    for (int i = p; i <= last; ++i) all &= reuse[i];
+    for (int i = p; i <= last; ++i) out[i] = last > p ? all : reuse[i];
+    p = last + 1;
+  }
+  return DITA_OK;
+}
+
+// Compose partitions first..last (validated by the caller: all valid, no
+// group straddling the range) into one group state in slot `first`.
+int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, int* launched) {
+  // `first` leads its group: no group straddles the range and first is in it.
+  dita::MergeSrc src;
+  int n = 0;
+  int64_t oldest = c->stamp[first];
+  for (int p = first; p <= last; ++p)
+    if (c->group[p] == p) {
+      src.o[n] = slot_o(c, p);
+      src.lse[n] = slot_lse(c, p);
+      ++n;
+      if (c->stamp[p] < oldest) oldest = c->stamp[p];
+    }
+  if (n > 1) {
+    // In place: the output is source 0 (slot `first`); each lane reads its
+    // elements of every source before it writes them.
+    const dita_shape& s = c->shape;
+    const int64_t rows = int64_t(s.B) * s.H * s.Nq;
+    const int st = hip_status(
+        dita::launch_merge(s.dtype, s.D, rows, n, src, slot_o(c, first), slot_lse(c, first), stream));
+    if (st) return st;
+  }
+  for (int p = first; p <= last; ++p) {
+    c->group[p] = int16_t(first);
+    c->valid[p] = 1;
+    c->stamp[p] = oldest;
+  }
+  if (launched) *launched = n > 1 ? 1 : 0;
+  return DITA_OK;
+}
+
+int ensure_events(dita_state_cache* c) {
+  int st;
+  if (!c->ev_fork && (st = hip_status(hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming))))
+    return st;
+  if (!c->ev_join && (st = hip_status(hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming))))
+    return st;
+  return DITA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,7 +200,7 @@ const char* dita_status_str(int status) {
 
 int dita_last_hip_error(void) { return g_last_hip_error; }
 
-int dita_version(void) { return 100; }
+int dita_version(void) { return 110; }
 
 int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
                       int64_t nk, void* o_p, float* lse_p, void* stream) {
@@ -184,15 +259,23 @@ int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P
   c->o_bytes = state_o_bytes(*shape);
   c->lse_offset = align256(c->o_bytes);
   c->slot_stride = c->lse_offset + align256(state_lse_bytes(*shape));
-  std::memset(c->valid, 0, sizeof(c->valid));
-  for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) c->stamp[p] = -1;
+  for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) reset_slot(c, p);
+  c->ev_fork = nullptr;
+  c->ev_join = nullptr;
   *out = c;
   return DITA_OK;
 }
 
 int dita_state_cache_free(dita_state_cache* cache) {
+  if (!cache) return DITA_OK;
+  int st = DITA_OK;
+  for (hipEvent_t e : {cache->ev_fork, cache->ev_join})
+    if (e) {
+      const int s2 = hip_status(hipEventDestroy(e));
+      if (!st) st = s2;
+    }
   delete cache;
-  return DITA_OK;
+  return st;
 }
 
 int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse) {
@@ -209,6 +292,7 @@ int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const 
   if (st) return st;
   if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
   if (step < 0) return DITA_ERR_ARG;
+  if (cache->group[p] != p || group_last(cache, p) != p) return DITA_ERR_STATE;
   const size_t lb = state_lse_bytes(cache->shape);
   if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
       overlaps(lse, lb, cache->base, cache->bytes))
@@ -225,7 +309,7 @@ int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* 
   int st = check_slot(cache, p);
   if (st) return st;
   if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
-  if (!cache->valid[p]) return DITA_ERR_STATE;
+  if (!cache->valid[p] || cache->group[p] != p) return DITA_ERR_STATE;
   const size_t lb = state_lse_bytes(cache->shape);
   if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
       overlaps(lse, lb, cache->base, cache->bytes))
@@ -237,16 +321,13 @@ int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* 
 int dita_state_cache_invalidate(dita_state_cache* cache, int p) {
   if (!cache) return DITA_ERR_ARG;
   if (p == -1) {
-    for (int i = 0; i < cache->P; ++i) {
-      cache->valid[i] = 0;
-      cache->stamp[i] = -1;
-    }
+    for (int i = 0; i < cache->P; ++i) reset_slot(cache, i);
     return DITA_OK;
   }
   const int st = check_slot(cache, p);
   if (st) return st;
-  cache->valid[p] = 0;
-  cache->stamp[p] = -1;
+  const int first = cache->group[p], last = group_last(cache, first);
+  for (int i = first; i <= last; ++i) reset_slot(cache, i);
   return DITA_OK;
 }
 
@@ -254,7 +335,7 @@ int dita_state_cache_info(const dita_state_cache* cache, int p, int* valid, int6
   const int st = check_slot(cache, p);
   if (st) return st;
   if (valid) *valid = cache->valid[p];
-  if (stamp) *stamp = cache->stamp[p];
+  if (stamp) *stamp = cache->stamp[cache->group[p]];
   return DITA_OK;
 }
 
@@ -262,6 +343,78 @@ int dita_state_cache_shape(const dita_state_cache* cache, dita_shape* shape, int
   if (!cache) return DITA_ERR_ARG;
   if (shape) *shape = cache->shape;
   if (P) *P = cache->P;
+  return DITA_OK;
+}
+
+int dita_state_cache_compose(dita_state_cache* cache, int first, int last, void* stream) {
+  if (!cache) return DITA_ERR_ARG;
+  if (first < 0 || last < first || last >= cache->P) return DITA_ERR_ARG;
+  for (int p = first; p <= last; ++p) {
+    if (!cache->valid[p]) return DITA_ERR_STATE;
+    if (cache->group[p] < first || group_last(cache, cache->group[p]) > last) return DITA_ERR_ARG;
+  }
+  return compose_range(cache, first, last, static_cast<hipStream_t>(stream), nullptr);
+}
+
+int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse, void* stream,
+                                  int* n_launched) {
+  if (!cache || !reuse) return DITA_ERR_ARG;
+  for (int p = 0; p < cache->P; ++p) {
+    if (reuse[p] > 1) return DITA_ERR_ARG;
+    if (reuse[p] && !cache->valid[p]) return DITA_ERR_STATE;
+  }
+  int first[DITA_MAX_PARTITIONS], last[DITA_MAX_PARTITIONS], n = 0;
+  for (int p = 0; p < cache->P;) {
+    if (!reuse[p]) {
+      ++p;
+      continue;
+    }
+    int a = p, b = p;
+    while (b + 1 < cache->P && reuse[b + 1]) ++b;
+    p = b + 1;
+    // Groups that reach outside the run will be recomputed whole: leave them out.
+    if (cache->group[a] < a) a = group_last(cache, cache->group[a]) + 1;
+    if (b >= a && group_last(cache, cache->group[b]) > b) b = cache->group[b] - 1;
+    if (a < b && !(cache->group[a] == a && group_last(cache, a) == b)) {
+      first[n] = a;
+      last[n] = b;
+      ++n;
+    }
+  }
+  int launched = 0;
+  for (int i = 0; i < n; ++i) {
+    int l = 0;
+    const int st = compose_range(cache, first[i], last[i], static_cast<hipStream_t>(stream), &l);
+    if (st) return st;
+    launched += l;
+  }
+  if (n_launched) *n_launched = launched;
+  return DITA_OK;
+}
+
+int dita_state_cache_group(const dita_state_cache* cache, int p, int* first, int* last) {
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  if (first) *first = cache->group[p];
+  if (last) *last = group_last(cache, cache->group[p]);
+  return DITA_OK;
+}
+
+int dita_state_cache_live(const dita_state_cache* cache, int* live) {
+  if (!cache || !live) return DITA_ERR_ARG;
+  int n = 0;
+  for (int p = 0; p < cache->P; ++p) n += (cache->group[p] == p && cache->valid[p]) ? 1 : 0;
+  *live = n;
+  return DITA_OK;
+}
+
+int dita_state_cache_effective_mask(const dita_state_cache* cache, const uint8_t* reuse,
+                                    uint8_t* out) {
+  if (!cache || !reuse || !out) return DITA_ERR_ARG;
+  uint8_t tmp[DITA_MAX_PARTITIONS];
+  const int st = effective_mask(cache, reuse, tmp);
+  if (st) return st;
+  std::memcpy(out, tmp, size_t(cache->P));
   return DITA_OK;
 }
 
@@ -277,10 +430,19 @@ int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t
 int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
                    const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
                    int64_t step, void* o, float* lse, void* stream, dita_step_info* info) {
+  return dita_attn_step_ex(cache, q, k_list, v_list, nk_list, reuse_mask, step, o, lse, stream,
+                           nullptr, info);
+}
+
+int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const* k_list,
+                      const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
+                      int64_t step, void* o, float* lse, void* stream, const dita_step_opts* opts,
+                      dita_step_info* info) {
   if (!cache || !k_list || !v_list || !nk_list || !reuse_mask) return DITA_ERR_ARG;
   int st;
   if ((st = check_dev(q)) || (st = check_dev(o)) || (st = check_dev(lse))) return st;
   if (step < 0) return DITA_ERR_ARG;
+  if (opts && (opts->reserved != 0 || opts->min_premerge < 0)) return DITA_ERR_ARG;
   const dita_shape& s = cache->shape;
   const int P = cache->P;
   const size_t ob = cache->o_bytes, lb = state_lse_bytes(s);
@@ -288,49 +450,85 @@ int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_
       overlaps(q, ob, cache->base, cache->bytes) || overlaps(o, ob, lse, lb))
     return DITA_ERR_ARG;
 
+  uint8_t reuse[DITA_MAX_PARTITIONS];
+  if ((st = effective_mask(cache, reuse_mask, reuse))) return st;
   dita::AttnJobs jobs;
   int n_fresh = 0;
   double fresh_keys = 0.0;
   for (int p = 0; p < P; ++p) {
-    if (reuse_mask[p] > 1) return DITA_ERR_ARG;
-    if (reuse_mask[p]) {
-      if (!cache->valid[p]) return DITA_ERR_STATE;
-      continue;
-    }
+    if (reuse[p]) continue;
     if ((st = check_dev(k_list[p])) || (st = check_dev(v_list[p]))) return st;
     if (!nk_ok(s, nk_list[p])) return DITA_ERR_SHAPE;
     jobs.job[n_fresh++] = dita::AttnJob{k_list[p], v_list[p], slot_o(cache, p), slot_lse(cache, p),
                                         nk_list[p]};
     fresh_keys += double(nk_list[p]);
   }
+  // Reused group states (leaders) and fresh states, in partition order.
+  int reused_heads[DITA_MAX_PARTITIONS], n_reused_heads = 0;
+  for (int p = 0; p < P; ++p)
+    if (reuse[p] && cache->group[p] == p) reused_heads[n_reused_heads++] = p;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipStream_t side = opts ? static_cast<hipStream_t>(opts->side_stream) : nullptr;
+  const int min_pre = opts && opts->min_premerge > 2 ? opts->min_premerge : 2;
+  const bool premerge = side && side != hs && n_fresh > 0 && n_reused_heads >= min_pre;
+  if (premerge && (st = ensure_events(cache))) return st;
+
   if (info && info->ev_begin && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_begin), hs))))
     return st;
+  const int64_t rows = int64_t(s.B) * s.H * s.Nq;
+  if (premerge) {
+    // The side stream starts after everything already on `stream` (earlier
+    // writers of the reused slots and users of o/lse) and merges the reused
+    // states into (o, lse) while the fresh attention runs.
+    dita::MergeSrc pre;
+    for (int i = 0; i < n_reused_heads; ++i) {
+      pre.o[i] = slot_o(cache, reused_heads[i]);
+      pre.lse[i] = slot_lse(cache, reused_heads[i]);
+    }
+    if ((st = hip_status(hipEventRecord(cache->ev_fork, hs))) ||
+        (st = hip_status(hipStreamWaitEvent(side, cache->ev_fork, 0))) ||
+        (st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_reused_heads, pre, o, lse, side))) ||
+        (st = hip_status(hipEventRecord(cache->ev_join, side))))
+      return st;
+  }
   if (n_fresh > 0 && (st = hip_status(launch_attn(s, q, jobs, n_fresh, hs)))) return st;
   if (info && info->ev_attn_end &&
       (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_attn_end), hs))))
     return st;
+  // Recomputed groups dissolve; fresh slots take this step's stamp.
   for (int p = 0; p < P; ++p)
-    if (!reuse_mask[p]) {
+    if (!reuse[p]) {
       cache->valid[p] = 1;
       cache->stamp[p] = step;
+      cache->group[p] = int16_t(p);
     }
 
   dita::MergeSrc src;
-  for (int p = 0; p < P; ++p) {
-    src.o[p] = slot_o(cache, p);
-    src.lse[p] = slot_lse(cache, p);
+  int n_src = 0;
+  if (premerge) {
+    if ((st = hip_status(hipStreamWaitEvent(hs, cache->ev_join, 0)))) return st;
+    src.o[n_src] = o;  // the pre-merged reused states; the merge writes it in place
+    src.lse[n_src] = lse;
+    ++n_src;
   }
-  const int64_t rows = int64_t(s.B) * s.H * s.Nq;
-  if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, P, src, o, lse, hs)))) return st;
+  for (int p = 0; p < P; ++p) {
+    if (cache->group[p] != p || (premerge && reuse[p])) continue;
+    src.o[n_src] = slot_o(cache, p);
+    src.lse[n_src] = slot_lse(cache, p);
+    ++n_src;
+  }
+  if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_src, src, o, lse, hs)))) return st;
   if (info && info->ev_end && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_end), hs))))
     return st;
   if (info) {
     info->n_fresh = n_fresh;
     info->n_reused = P - n_fresh;
     info->fresh_flops = 4.0 * double(s.B) * s.H * double(s.Nq) * fresh_keys * s.D;
-    info->merge_bytes = double(P + 1) * double(ob + lb);
+    info->merge_sources = n_src;
+    info->merge_bytes = double(n_src + 1) * double(ob + lb);
+    info->premerge_sources = premerge ? n_reused_heads : 0;
+    info->premerge_bytes = premerge ? double(n_reused_heads + 1) * double(ob + lb) : 0.0;
   }
   return DITA_OK;
 }

@@ -224,6 +224,50 @@ def test_attn_step_validation_before_launch():
     lib.dita_state_cache_free(h)
 
 
+def test_group_calls_host_only():
+    """Group metadata calls on an empty cache: every partition is a group of one,
+    and composition of states that do not exist is refused before any launch."""
+    shape = dita.Shape(1, 2, 64, dita.DITA_BF16, 64, 0.0)
+    h = _cache(shape, 5)
+    a, b = ctypes.c_int(), ctypes.c_int()
+    for p in range(5):
+        assert lib.dita_state_cache_group(h, p, ctypes.byref(a), ctypes.byref(b)) == 0
+        assert (a.value, b.value) == (p, p)
+    assert lib.dita_state_cache_group(h, 5, None, None) == dita.DITA_ERR_ARG
+    live = ctypes.c_int()
+    assert lib.dita_state_cache_live(h, ctypes.byref(live)) == 0 and live.value == 0
+    assert lib.dita_state_cache_live(h, None) == dita.DITA_ERR_ARG
+    for first, last in [(2, 1), (-1, 2), (0, 5)]:
+        assert lib.dita_state_cache_compose(h, first, last, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_compose(h, 1, 3, None) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_compose(None, 0, 1, None) == dita.DITA_ERR_ARG
+    m = (ctypes.c_uint8 * 5)(0, 0, 0, 0, 0)
+    out = (ctypes.c_uint8 * 5)(9, 9, 9, 9, 9)
+    assert lib.dita_state_cache_effective_mask(h, m, out) == 0 and list(out) == [0] * 5
+    assert lib.dita_state_cache_effective_mask(h, (ctypes.c_uint8 * 5)(0, 1, 0, 0, 0), out) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_effective_mask(h, (ctypes.c_uint8 * 5)(0, 3, 0, 0, 0), out) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_effective_mask(h, None, out) == dita.DITA_ERR_ARG
+    lib.dita_state_cache_free(h)
+
+
+def test_attn_step_ex_validates_options():
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    h = _cache(shape, 2)
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), 2)
+    q, o, l = FAKE_DEV + n + 4096, FAKE_DEV + n + (1 << 20), FAKE_DEV + n + (2 << 20)
+    ks = (ctypes.c_void_p * 2)(FAKE_DEV + n + (3 << 20), FAKE_DEV + n + (4 << 20))
+    nk = (ctypes.c_int64 * 2)(64, 64)
+    zeros = (ctypes.c_uint8 * 2)(0, 0)
+    for side, minp, res in [(FAKE_DEV, 0, 1), (FAKE_DEV, -1, 0)]:
+        opts = dita.StepOpts(side, minp, res)
+        assert lib.dita_attn_step_ex(h, q, ks, ks, nk, zeros, 0, o, l, None, ctypes.byref(opts),
+                                     None) == dita.DITA_ERR_ARG
+    opts = dita.StepOpts(FAKE_DEV, 0, 0)
+    assert lib.dita_attn_step_ex(h, q, ks, ks, nk, (ctypes.c_uint8 * 2)(0, 1), 0, o, l, None,
+                                 ctypes.byref(opts), None) == dita.DITA_ERR_STATE
+    lib.dita_state_cache_free(h)
+
+
 def test_event_helpers_validate():
     assert lib.dita_event_create(None) == dita.DITA_ERR_ARG
     assert lib.dita_event_record(None, None) == dita.DITA_ERR_ARG

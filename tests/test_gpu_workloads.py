@@ -17,6 +17,7 @@ from gpu_util import assert_state_close, say, to_dev, to_host
 from oracle import Plan as OraclePlan
 from oracle import StateCache as OracleCache
 from oracle import attn_step as oracle_step
+from oracle import compose_runs as oracle_compose_runs
 from oracle import full_attention
 from oracle import plan_mask as oracle_mask
 from workloads import Inputs, split_parts
@@ -40,7 +41,10 @@ def sample_rows(wl):
     return heads, rows
 
 
-def run_schedule(wl, dev, steps=None, seed=0):
+def run_schedule(wl, dev, steps=None, seed=0, compose_ahead=False):
+    """Run the workload's schedule on both sides.  With ``compose_ahead`` the
+    runs of partitions the next step reuses are composed into groups after
+    every step (the benchmark's default pipeline), on both sides."""
     import torch
     import partial_state_reuse_amd as dita
     steps = wl.steps if steps is None else steps
@@ -80,6 +84,18 @@ def run_schedule(wl, dev, steps=None, seed=0):
             assert cache.info(int(p)) == (True, s)
         worst = [max(worst[0], eo), max(worst[1], el)]
         say(f"[{wl.name}] step {s}: fresh {nf}/{wl.P}  O err {eo:.2e}  LSE err {el:.2e}")
+        if compose_ahead and s + 1 < steps:
+            nxt = dita.dita_plan_mask(plan, s + 1, cache)
+            assert np.array_equal(nxt, oracle_mask(ref_plan, s + 1, ref_cache.valid))
+            assert cache.compose_runs(nxt) == oracle_compose_runs(ref_cache, nxt)
+            for p in ref_cache.leaders():
+                first, last = ref_cache.group_range(p)
+                assert cache.group(p) == (first, last)
+                if last > first:
+                    so, sl = cache.slot(p)
+                    ro, rl = ref_cache.slots[p]
+                    assert_state_close(sel(to_host(so)), sel(to_host(sl)), ro, rl, wl.dtype,
+                                       f"{wl.name} step {s} group [{first}, {last}]")
     return worst, fresh_total, (cache, q_dev, inp)
 
 
@@ -92,15 +108,16 @@ def test_single_step_workload(dev, name):
         assert fresh == expect_fresh[name]
 
 
-def test_dit75k_anchor_schedule(dev):
+@pytest.mark.parametrize("compose_ahead", [False, True])
+def test_dit75k_anchor_schedule(dev, compose_ahead):
     wl = workloads.get("dit75k_bf16")
-    worst, fresh, _ = run_schedule(wl, dev)
+    worst, fresh, _ = run_schedule(wl, dev, compose_ahead=compose_ahead)
     assert fresh == 56
 
 
 def test_dit75k_ramp50_schedule(dev):
     wl = workloads.get("dit75k_ramp50")
-    worst, fresh, _ = run_schedule(wl, dev)
+    worst, fresh, _ = run_schedule(wl, dev, compose_ahead=True)
     assert fresh == 282
 
 

@@ -58,8 +58,8 @@ MUTATIONS = [
      "o = np.sum(w[..., None] * outs, axis=0)"),
     ("attention.py", "all-neutral rows merge to LSE 0",
      "lse = np.where(empty, -np.inf,", "lse = np.where(empty, 0.0,"),
-    ("cache.py", "reuse mask read inverted", "        if not reuse[p]:\n",
-     "        if reuse[p]:\n"),
+    ("cache.py", "reuse mask read inverted", "        if not reuse[p]:\n            cache.store(",
+     "        if reuse[p]:\n            cache.store("),
     ("cache.py", "fresh state from the wrong V partition",
      "partial_state(q, k_parts[p], v_parts[p], scale)",
      "partial_state(q, k_parts[p], v_parts[0], scale)"),
@@ -78,7 +78,14 @@ MUTATIONS = [
     ("cache.py", "group range one short", "while last + 1 < self.P and self.group[last + 1] == first:",
      "while last + 2 < self.P and self.group[last + 1] == first:"),
     ("cache.py", "reuse of an empty slot not rejected",
-     "if reuse[p] and not cache.valid[p]:", "if False:"),
+     "        if reuse[p] and not cache.valid[p]:\n            raise RuntimeError(f\"partition {p} is marked reuse but its slot is empty\")\n    reuse = effective_reuse",
+     "        if False:\n            raise RuntimeError(f\"partition {p} is marked reuse but its slot is empty\")\n    reuse = effective_reuse"),
+    ("cache.py", "compose-ahead run ends one short",
+     "        while p + 1 < cache.P and reuse[p + 1]:\n",
+     "        while p + 2 < cache.P and reuse[p + 1]:\n"),
+    ("cache.py", "compose-ahead keeps groups reaching outside the run",
+     "if cache.group_range(i)[0] >= a and cache.group_range(i)[1] <= b]",
+     "if cache.group_range(i)[0] >= a]"),
     ("planner.py", "SplitMix64 multiplier typo", "0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
     ("planner.py", "SplitMix64 shift", "z = ((z ^ (z >> 30))", "z = ((z ^ (z >> 31))"),
     ("planner.py", "SplitMix64 output before the gamma step",
