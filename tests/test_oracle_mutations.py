@@ -170,6 +170,7 @@ def test_unmodified_copy_passes_every_pin(tmp_path):
     modules = sorted({m for ms in PINS.values() for m in ms})
     failed, n_run = _run_pins(tmp_path, modules)
     assert failed == []
+    print(f"{n_run} pin cases")
     assert n_run >= 70, n_run   # every parametrised pin case ran
 
 
