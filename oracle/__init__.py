@@ -24,6 +24,9 @@ attention  partial attention state, LSE merge, full attention (float64).
 cache      the per-partition state cache, group composition and one
            compute-or-reuse rank-step.
 planner    the reuse-mask planner and its SplitMix64 integer generator.
+error_planner  contribution weights, local state change and the group-wise,
+           error-budgeted planner ("Error Modeling", "Online Prediction",
+           "Group-wise Strategy" of the planner section).
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 closed forms, textbook/library routines it does not itself call (scipy's
@@ -35,6 +38,7 @@ which the pages give no numbers for.
 
 from .attention import full_attention, merge_states, partial_state, softmax_scale
 from .cache import StateCache, attn_step, compose_runs, effective_reuse
+from .error_planner import ErrorPlanner, contributions, state_change
 from .planner import (
     POLICY_DIST,
     POLICY_KNEAREST,
@@ -55,6 +59,9 @@ __all__ = [
     "attn_step",
     "effective_reuse",
     "compose_runs",
+    "ErrorPlanner",
+    "contributions",
+    "state_change",
     "Plan",
     "SplitMix64",
     "plan_mask",

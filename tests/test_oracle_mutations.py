@@ -28,6 +28,7 @@ PINS = {
     "attention.py": ["test_oracle_attention", "test_oracle_merge"],
     "cache.py": ["test_oracle_merge", "test_oracle_groups"],
     "planner.py": ["test_oracle_planner", "test_abi"],
+    "error_planner.py": ["test_oracle_error_planner"],
 }
 
 # (file, what the mistake is, text in the oracle, replacement)
@@ -86,6 +87,22 @@ MUTATIONS = [
     ("cache.py", "compose-ahead keeps groups reaching outside the run",
      "if cache.group_range(i)[0] >= a and cache.group_range(i)[1] <= b]",
      "if cache.group_range(i)[0] >= a]"),
+    ("error_planner.py", "contribution without the merged LSE",
+     "w[ok] = np.exp(lp[ok] - lse[ok])", "w[ok] = np.exp(lp[ok])"),
+    ("error_planner.py", "contribution averaged over partitions, not rows",
+     "out[p] = float(np.sum(w)) / lse.size", "out[p] = float(np.sum(w)) / len(lse_parts)"),
+    ("error_planner.py", "state change not relative", "return num / den", "return num"),
+    ("error_planner.py", "growth counted from the stamp step itself",
+     "for t in range(int(stamp[p]) + 1, step + 1):", "for t in range(int(stamp[p]), step + 1):"),
+    ("error_planner.py", "prediction peeks at the planned step",
+     "seen = sorted(u for u in self.delta if u <= step - 1)",
+     "seen = sorted(u for u in self.delta if u <= step)"),
+    ("error_planner.py", "local partition inside its group's decision",
+     "members = [p for p in range(a, b + 1) if p != q]", "members = [p for p in range(a, b + 1)]"),
+    ("error_planner.py", "groups taken in decreasing error",
+     "candidates.sort(key=lambda c: (c[0], c[1]))", "candidates.sort(key=lambda c: (-c[0], c[1]))"),
+    ("error_planner.py", "error without the weight", "err[p] = self.weights[p] * growth",
+     "err[p] = growth"),
     ("planner.py", "SplitMix64 multiplier typo", "0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
     ("planner.py", "SplitMix64 shift", "z = ((z ^ (z >> 30))", "z = ((z ^ (z >> 31))"),
     ("planner.py", "SplitMix64 output before the gamma step",
