@@ -327,6 +327,76 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
                       dita_step_info* info);
 
 /*
+ * Planner statistics.  Page section: 1. Anchor-Guided Selection Planner --
+ * Error Modeling (partition importance w), Anchor Steps (w refreshed on
+ * anchors) and Online Prediction (the change of the always-computed local
+ * state stands in for the remote ones).
+ *
+ * dita_state_contrib: w_out[p] = mean over the B*H*Nq rows of
+ *   exp(lse_list[p] - lse), the share of partition p in the merged softmax
+ *   (rows where either LSE is -inf count 0).  lse_list: host array of P device
+ *   pointers [B, H, Nq] float32; lse: the merged LSE; w_out: device, P
+ *   doubles.  fp64 accumulation in a fixed order (deterministic).
+ * dita_state_cache_contrib: the same over the cache's P slots (every slot must
+ *   hold its own state -- no composed groups -- else DITA_ERR_STATE), with
+ *   `lse` the LSE the step merged them into.
+ * dita_state_change: out[0] = sum (o_new - o_prev)^2, out[1] = sum o_prev^2,
+ *   out[2] = sqrt(out[0] / out[1]) (0 when both sums are 0, +inf when only
+ *   out[1] is) over all B*H*Nq*D elements, fp64 (the order of the final
+ *   per-workgroup additions is not fixed).  roll != 0 also copies (o_new,
+ *   lse_new) over (o_prev, lse_prev) in the same pass.  out: device, 3
+ *   doubles.  o_new/o_prev: device [B, H, Nq, D] dtype; lse_new/lse_prev:
+ *   device [B, H, Nq] float32 (read/written only when rolling; may be NULL
+ *   otherwise).  The new and previous buffers must not overlap.
+ */
+int dita_state_contrib(const dita_shape* shape, int P, const float* const* lse_list,
+                       const float* lse, double* w_out, void* stream);
+int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, double* w_out,
+                             void* stream);
+int dita_state_change(const dita_shape* shape, const void* o_new, const float* lse_new,
+                      void* o_prev, float* lse_prev, int roll, double* out, void* stream);
+
+/*
+ * Error-guided planner (host only, float64).  Page section: 1. Anchor-Guided
+ * Selection Planner (Error Modeling, Anchor Steps, Online Prediction,
+ * Group-wise Strategy).  The page prints no formula; this one is:
+ *   err_p = w_p * sum over t in (stamp_p, step] of delta~_t, where delta~_t
+ *           is the change observed at the latest step <= min(t, step - 1), or
+ *           the earliest observed change when none precedes t;
+ *   groups = contiguous blocks of group_size partitions; a group's error is
+ *           the sum over its members other than the local partition;
+ *   the groups are taken in increasing (error, group index) order and reused
+ *   while the running sum stays <= budget; the others are computed fresh.
+ * All partitions are fresh on an anchor step (anchor_period > 0 and
+ * step % anchor_period == 0), before weights are set, and before a change
+ * observed at a step < `step` exists; the local partition is always fresh; a
+ * group with an invalid slot is fresh.  Sums run in ascending index order.
+ */
+typedef struct {
+  int32_t P;              /* partitions, 1..DITA_MAX_PARTITIONS                */
+  int32_t q;              /* the local partition                               */
+  int32_t group_size;     /* partitions per group, >= 1                        */
+  int32_t anchor_period;  /* > 0: every anchor_period-th step is all fresh     */
+  double budget;          /* total estimated error allowed to be reused, >= 0  */
+} dita_error_plan;
+
+typedef struct dita_planner dita_planner;
+
+int dita_planner_create(dita_planner** out, const dita_error_plan* plan);
+int dita_planner_free(dita_planner* planner);
+/* w: host array of P finite, non-negative weights (e.g. from dita_state_contrib). */
+int dita_planner_set_weights(dita_planner* planner, const double* w);
+/* The local state's change measured at `step` (finite, >= 0); replaces an earlier value. */
+int dita_planner_observe(dita_planner* planner, int64_t step, double change);
+/* valid, stamp: host arrays of P entries (stamp <= step where valid); reuse_out: P
+ * bytes (1 = reuse); err_out: P doubles or NULL. */
+int dita_planner_mask(const dita_planner* planner, int64_t step, const uint8_t* valid,
+                      const int64_t* stamp, uint8_t* reuse_out, double* err_out);
+/* The same with valid/stamp read from the cache (a group member carries its group's stamp). */
+int dita_planner_mask_cache(const dita_planner* planner, const dita_state_cache* cache,
+                            int64_t step, uint8_t* reuse_out, double* err_out);
+
+/*
  * Timing helpers (thin wrappers over HIP events, for benchmarks that time the
  * kernels on the stream they run on).
  */

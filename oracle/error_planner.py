@@ -86,11 +86,15 @@ class ErrorPlanner:
         self.delta: Dict[int, float] = {}
 
     def set_weights(self, w: Sequence[float]) -> None:
-        if len(w) != self.P:
-            raise ValueError("need P weights")
+        if len(w) != self.P or not all(math.isfinite(float(x)) and float(x) >= 0.0 for x in w):
+            raise ValueError("need P finite, non-negative weights")
         self.weights = [float(x) for x in w]
 
     def observe(self, step: int, delta: float) -> None:
+        """Record the local state change measured at ``step`` (a later call for
+        the same step replaces it)."""
+        if step < 0 or not (math.isfinite(float(delta)) and float(delta) >= 0.0):
+            raise ValueError("need step >= 0 and a finite, non-negative change")
         self.delta[int(step)] = float(delta)
 
     def _delta_at(self, t: int, step: int) -> float:

@@ -64,6 +64,11 @@ class StepInfo(ctypes.Structure):
                 ("premerge_sources", ctypes.c_int32), ("premerge_bytes", ctypes.c_double)]
 
 
+class ErrorPlan(ctypes.Structure):
+    _fields_ = [("P", ctypes.c_int32), ("q", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("anchor_period", ctypes.c_int32), ("budget", ctypes.c_double)]
+
+
 class StepOpts(ctypes.Structure):
     _fields_ = [("side_stream", ctypes.c_void_p), ("min_premerge", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
@@ -109,6 +114,17 @@ def _load() -> ctypes.CDLL:
         "dita_attn_step_ex": (i32, [vp, vp, pvp, pvp, ctypes.POINTER(i64),
                                     ctypes.POINTER(ctypes.c_uint8), i64, vp, vp, vp,
                                     ctypes.POINTER(StepOpts), ctypes.POINTER(StepInfo)]),
+        "dita_state_contrib": (i32, [ctypes.POINTER(Shape), i32, pvp, vp, vp, vp]),
+        "dita_state_cache_contrib": (i32, [vp, vp, vp, vp]),
+        "dita_state_change": (i32, [ctypes.POINTER(Shape), vp, vp, vp, vp, i32, vp, vp]),
+        "dita_planner_create": (i32, [pvp, ctypes.POINTER(ErrorPlan)]),
+        "dita_planner_free": (i32, [vp]),
+        "dita_planner_set_weights": (i32, [vp, ctypes.POINTER(ctypes.c_double)]),
+        "dita_planner_observe": (i32, [vp, i64, ctypes.c_double]),
+        "dita_planner_mask": (i32, [vp, i64, ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(i64),
+                                    ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_double)]),
+        "dita_planner_mask_cache": (i32, [vp, vp, i64, ctypes.POINTER(ctypes.c_uint8),
+                                          ctypes.POINTER(ctypes.c_double)]),
         "dita_event_create": (i32, [pvp]),
         "dita_event_destroy": (i32, [vp]),
         "dita_event_record": (i32, [vp, vp]),
@@ -323,6 +339,15 @@ class StateCache:
                                                   ctypes.byref(n)), "dita_state_cache_compose_runs")
         return n.value
 
+    def contrib(self, lse, w=None, stream=None):
+        """Device float64 [P]: each slot's share exp(LSE_p - lse) averaged over rows."""
+        torch = _torch()
+        if w is None:
+            w = torch.empty(self.P, dtype=torch.float64, device=self.buffer.device)
+        _check(_lib.dita_state_cache_contrib(self.handle, _ptr(lse), _ptr(w), _stream(lse, stream)),
+               "dita_state_cache_contrib")
+        return w
+
     def group(self, p: int):
         """(first, last) of the group holding partition p."""
         a, b = ctypes.c_int(), ctypes.c_int()
@@ -398,6 +423,78 @@ def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reu
         _check(_lib.dita_attn_step_ex(*args, ctypes.byref(opts), ctypes.byref(info)),
                "dita_attn_step_ex")
     return o, lse, info
+
+
+def dita_state_contrib(lse_list: Sequence, lse, w=None, stream=None):
+    """Device float64 [P]: mean over rows of exp(LSE_p - LSE) for each state's LSE."""
+    torch = _torch()
+    P = len(lse_list)
+    B, H, Nq = lse.shape
+    if w is None:
+        w = torch.empty(P, dtype=torch.float64, device=lse.device)
+    shape = Shape(B, H, 64, DITA_F32, Nq, 0.0)   # only B, H, Nq matter here
+    _check(_lib.dita_state_contrib(ctypes.byref(shape), P, _ptr_array([_ptr(x) for x in lse_list]),
+                                   _ptr(lse), _ptr(w), _stream(lse, stream)), "dita_state_contrib")
+    return w
+
+
+def dita_state_change(o_new, o_prev, lse_new=None, lse_prev=None, roll: bool = False, out=None,
+                      stream=None):
+    """Device float64 [3]: sum (new - prev)^2, sum prev^2 and the relative change
+    sqrt of their ratio; with ``roll`` the new state is also copied over prev."""
+    torch = _torch()
+    if o_new.shape != o_prev.shape or o_new.dtype != o_prev.dtype:
+        raise ValueError("states must share shape and dtype")
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=o_new.device)
+    shape = make_shape(o_new)
+    _check(_lib.dita_state_change(ctypes.byref(shape), _ptr(o_new), _ptr(lse_new), _ptr(o_prev),
+                                  _ptr(lse_prev), int(bool(roll)), _ptr(out), _stream(o_new, stream)),
+           "dita_state_change")
+    return out
+
+
+class ErrorPlanner:
+    """The library's error-guided, group-wise planner (dita_planner_*)."""
+
+    def __init__(self, P: int, q: int, group_size: int, budget: float, anchor_period: int = 0):
+        self.P = P
+        h = ctypes.c_void_p()
+        _check(_lib.dita_planner_create(ctypes.byref(h), ctypes.byref(
+            ErrorPlan(P, q, group_size, anchor_period, float(budget)))), "dita_planner_create")
+        self.handle = h.value
+
+    def set_weights(self, w: Sequence[float]):
+        arr = (ctypes.c_double * self.P)(*[float(x) for x in w])
+        _check(_lib.dita_planner_set_weights(self.handle, arr), "dita_planner_set_weights")
+
+    def observe(self, step: int, change: float):
+        _check(_lib.dita_planner_observe(self.handle, step, float(change)), "dita_planner_observe")
+
+    def mask(self, step: int, valid=None, stamp=None, cache: Optional["StateCache"] = None):
+        """(reuse uint8[P], estimated error float64[P]); metadata from ``cache`` or the arrays."""
+        out = (ctypes.c_uint8 * self.P)()
+        err = (ctypes.c_double * self.P)()
+        if cache is not None:
+            _check(_lib.dita_planner_mask_cache(self.handle, cache.handle, step, out, err),
+                   "dita_planner_mask_cache")
+        else:
+            v = (ctypes.c_uint8 * self.P)(*[int(x) for x in valid])
+            t = (ctypes.c_int64 * self.P)(*[int(x) for x in stamp])
+            _check(_lib.dita_planner_mask(self.handle, step, v, t, out, err), "dita_planner_mask")
+        return (np.frombuffer(bytes(out), dtype=np.uint8).copy(),
+                np.frombuffer(bytes(err), dtype=np.float64).copy())
+
+    def close(self):
+        if self.handle:
+            _lib.dita_planner_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Event:

@@ -533,6 +533,62 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
   return DITA_OK;
 }
 
+int dita_state_contrib(const dita_shape* shape, int P, const float* const* lse_list,
+                       const float* lse, double* w_out, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if (!lse_list) return DITA_ERR_ARG;
+  if ((st = check_dev(lse)) || (st = check_dev(w_out))) return st;
+  dita::LseList src;
+  for (int p = 0; p < P; ++p) {
+    if ((st = check_dev(lse_list[p]))) return st;
+    src.lse[p] = lse_list[p];
+  }
+  const int64_t rows = int64_t(shape->B) * shape->H * shape->Nq;
+  return hip_status(dita::launch_contrib(P, src, lse, rows, w_out, static_cast<hipStream_t>(stream)));
+}
+
+int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, double* w_out,
+                             void* stream) {
+  if (!cache) return DITA_ERR_ARG;
+  int st;
+  if ((st = check_dev(lse)) || (st = check_dev(w_out))) return st;
+  const float* lses[DITA_MAX_PARTITIONS];
+  for (int p = 0; p < cache->P; ++p) {
+    if (!cache->valid[p] || cache->group[p] != p || group_last(cache, p) != p) return DITA_ERR_STATE;
+    lses[p] = slot_lse(cache, p);
+  }
+  return dita_state_contrib(&cache->shape, cache->P, lses, lse, w_out, stream);
+}
+
+int dita_state_change(const dita_shape* shape, const void* o_new, const float* lse_new,
+                      void* o_prev, float* lse_prev, int roll, double* out, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_dev(o_new)) || (st = check_dev(o_prev)) || (st = check_dev(out))) return st;
+  if (roll != 0 && roll != 1) return DITA_ERR_ARG;
+  const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
+  if (overlaps(o_new, ob, o_prev, ob) || overlaps(out, 24, o_prev, ob) || overlaps(out, 24, o_new, ob))
+    return DITA_ERR_ARG;
+  if (roll) {
+    if ((st = check_dev(lse_new)) || (st = check_dev(lse_prev))) return st;
+    if (overlaps(lse_new, lb, lse_prev, lb) || overlaps(lse_prev, lb, o_new, ob) ||
+        overlaps(o_prev, ob, lse_new, lb) || overlaps(out, 24, lse_prev, lb))
+      return DITA_ERR_ARG;
+  }
+  return hip_status(dita::launch_change(shape->dtype, o_new, o_prev, ob, lse_new, lse_prev,
+                                        roll ? lb : 0, roll, out, static_cast<hipStream_t>(stream)));
+}
+
+int dita_planner_mask_cache(const dita_planner* planner, const dita_state_cache* cache,
+                            int64_t step, uint8_t* reuse_out, double* err_out) {
+  if (!cache) return DITA_ERR_ARG;
+  int64_t stamp[DITA_MAX_PARTITIONS];
+  for (int p = 0; p < cache->P; ++p) stamp[p] = cache->stamp[cache->group[p]];
+  return dita_planner_mask(planner, step, cache->valid, stamp, reuse_out, err_out);
+}
+
 int dita_event_create(void** event) {
   if (!event) return DITA_ERR_ARG;
   hipEvent_t e = nullptr;

@@ -46,6 +46,20 @@ struct MergeSrc {
 hipError_t launch_merge(int dtype, int D, int64_t rows, int P, const MergeSrc& src, void* o,
                         float* lse, hipStream_t stream);
 
+struct LseList {
+  const float* lse[kMaxParts];
+};
+
+// w[p] = mean over `rows` rows of exp(LSE_p - LSE) (fp64), one workgroup per partition.
+hipError_t launch_contrib(int P, const LseList& src, const float* lse, int64_t rows, double* w,
+                          hipStream_t stream);
+
+// out[0] = sum (new - prev)^2, out[1] = sum prev^2, out[2] = sqrt(out[0] / out[1]) over the
+// O elements (fp64); roll != 0 also copies the new state (O and LSE) over prev.
+hipError_t launch_change(int dtype, const void* o_new, void* o_prev, size_t o_bytes,
+                         const float* lse_new, float* lse_prev, size_t lse_bytes, int roll,
+                         double* out, hipStream_t stream);
+
 // Copy of one attention state (O bytes and LSE bytes, each a multiple of 4 bytes).
 hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,
                              size_t o_bytes, size_t lse_bytes, hipStream_t stream);

@@ -268,6 +268,92 @@ def test_attn_step_ex_validates_options():
     lib.dita_state_cache_free(h)
 
 
+def test_error_planner_matches_oracle_bit_for_bit():
+    """The C++ error-guided planner against the oracle's, on random weights,
+    observations (in any order, some replaced), stamps, validity, group sizes and
+    budgets: the masks must agree exactly and the error estimates to the bit."""
+    from oracle.error_planner import ErrorPlanner as OracleErrorPlanner
+    rng = np.random.default_rng(42)
+    n_reused = 0
+    for trial in range(3000):
+        P = int(rng.integers(1, 65))
+        q = int(rng.integers(0, P))
+        g = int(rng.integers(1, 6))
+        ap = int(rng.choice([0, 0, 3, 5, 7]))
+        budget = float(rng.choice([0.0, rng.uniform(0, 0.02), rng.uniform(0, 0.2), np.inf]))
+        ref = OracleErrorPlanner(P, q, g, budget, ap)
+        lib_pl = dita.ErrorPlanner(P, q, g, budget, ap)
+        if rng.random() < 0.95:
+            w = rng.dirichlet(np.ones(P) * 0.5)
+            ref.set_weights(list(w))
+            lib_pl.set_weights(list(w))
+        step = int(rng.integers(0, 40))
+        for _ in range(int(rng.integers(0, 8))):
+            t = int(rng.integers(0, 45))
+            d = float(rng.choice([0.0, rng.exponential(0.01)]))
+            ref.observe(t, d)
+            lib_pl.observe(t, d)
+        valid = (rng.random(P) < 0.9).astype(np.uint8)
+        stamp = np.where(valid == 1, rng.integers(0, step + 1, P), -1)
+        r_ref, e_ref = ref.mask(step, valid, stamp)
+        r_lib, e_lib = lib_pl.mask(step, valid, stamp)
+        assert np.array_equal(r_ref, r_lib), (trial, r_ref, r_lib)
+        assert np.array_equal(e_ref, e_lib), (trial, e_ref, e_lib)
+        n_reused += int(r_ref.sum())
+    assert n_reused > 1000          # the random plans do reuse
+
+
+def test_error_planner_validation():
+    bad = [(0, 0, 1, 0, 0.1), (4, 4, 1, 0, 0.1), (4, 0, 0, 0, 0.1), (4, 0, 1, -1, 0.1),
+           (4, 0, 1, 0, -0.5), (4, 0, 1, 0, float("nan"))]
+    h = ctypes.c_void_p()
+    for P, q, g, ap, b in bad:
+        assert lib.dita_planner_create(ctypes.byref(h), ctypes.byref(dita.ErrorPlan(P, q, g, ap, b))) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_create(None, ctypes.byref(dita.ErrorPlan(4, 0, 1, 0, 0.1))) == dita.DITA_ERR_ARG
+    pl = dita.ErrorPlanner(4, 0, 2, 0.1)
+    dbl = lambda *x: (ctypes.c_double * 4)(*x)
+    assert lib.dita_planner_set_weights(pl.handle, dbl(0.1, -0.1, 0.5, 0.5)) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_set_weights(pl.handle, dbl(0.1, float("inf"), 0.5, 0.5)) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_observe(pl.handle, -1, 0.1) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_observe(pl.handle, 2, float("nan")) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_observe(pl.handle, 2, -1.0) == dita.DITA_ERR_ARG
+    v = (ctypes.c_uint8 * 4)(1, 1, 1, 1)
+    out = (ctypes.c_uint8 * 4)()
+    t_bad = (ctypes.c_int64 * 4)(0, 0, 9, 0)        # a stamp after the planned step
+    assert lib.dita_planner_mask(pl.handle, 5, v, t_bad, out, None) == dita.DITA_ERR_ARG
+    v_bad = (ctypes.c_uint8 * 4)(1, 2, 1, 1)
+    t_ok = (ctypes.c_int64 * 4)(0, 0, 0, 0)
+    assert lib.dita_planner_mask(pl.handle, 5, v_bad, t_ok, out, None) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_mask(pl.handle, 5, v, t_ok, out, None) == 0
+    assert lib.dita_planner_free(None) == 0
+
+
+def test_stats_calls_validate_before_launch():
+    shape = dita.Shape(1, 2, 64, dita.DITA_BF16, 64, 0.0)
+    p = FAKE_DEV
+    arr = lambda *x: (ctypes.c_void_p * len(x))(*x)
+    l2 = arr(p, p + 4096)
+    assert lib.dita_state_contrib(ctypes.byref(shape), 0, l2, p + 8192, p + 16384, None) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_contrib(ctypes.byref(shape), 2, None, p + 8192, p + 16384, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_contrib(ctypes.byref(shape), 2, arr(p, p + 4), p + 8192, p + 16384, None) == dita.DITA_ERR_ALIGN
+    assert lib.dita_state_contrib(ctypes.byref(shape), 2, l2, p + 8192, None, None) == dita.DITA_ERR_ARG
+    o_bytes = 2 * 64 * 64 * 2
+    a, b, out = p, p + (1 << 20), p + (2 << 20)
+    assert lib.dita_state_change(ctypes.byref(shape), a, None, a + 256, None, 0, out, None) == dita.DITA_ERR_ARG  # overlap
+    assert lib.dita_state_change(ctypes.byref(shape), a, None, b, None, 2, out, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_change(ctypes.byref(shape), a, None, b, None, 1, out, None) == dita.DITA_ERR_ARG  # roll needs LSEs
+    assert lib.dita_state_change(ctypes.byref(shape), a, None, b, None, 0, a + 64, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_change(ctypes.byref(shape), a, None, b, None, 0, None, None) == dita.DITA_ERR_ARG
+    assert o_bytes < (1 << 20)
+    h = _cache(shape, 3)
+    assert lib.dita_state_cache_contrib(h, p + (64 << 20), p + (65 << 20), None) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_contrib(None, p, p, None) == dita.DITA_ERR_ARG
+    pl = dita.ErrorPlanner(3, 0, 1, 0.1)
+    r, e = pl.mask(3, cache=type("C", (), {"handle": h})())
+    assert list(r) == [0, 0, 0]
+    lib.dita_state_cache_free(h)
+
+
 def test_event_helpers_validate():
     assert lib.dita_event_create(None) == dita.DITA_ERR_ARG
     assert lib.dita_event_record(None, None) == dita.DITA_ERR_ARG

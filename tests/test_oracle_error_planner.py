@@ -165,3 +165,11 @@ def test_bad_parameters():
                dict(P=4, q=0, group_size=0, budget=0.1), dict(P=4, q=0, group_size=1, budget=-1.0)]:
         with pytest.raises(ValueError):
             ErrorPlanner(**kw)
+
+    pl = ErrorPlanner(P=3, q=0, group_size=1, budget=0.1)
+    for bad in ([0.5, 0.5], [0.5, -0.1, 0.6], [0.5, math.nan, 0.5], [math.inf, 0.0, 0.0]):
+        with pytest.raises(ValueError):
+            pl.set_weights(bad)
+    for step, d in ((-1, 0.1), (2, -0.1), (2, math.inf), (2, math.nan)):
+        with pytest.raises(ValueError):
+            pl.observe(step, d)

@@ -28,7 +28,7 @@ PINS = {
     "attention.py": ["test_oracle_attention", "test_oracle_merge"],
     "cache.py": ["test_oracle_merge", "test_oracle_groups"],
     "planner.py": ["test_oracle_planner", "test_abi"],
-    "error_planner.py": ["test_oracle_error_planner"],
+    "error_planner.py": ["test_oracle_error_planner", "test_abi"],
 }
 
 # (file, what the mistake is, text in the oracle, replacement)
