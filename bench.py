@@ -79,6 +79,17 @@ def parse():
     ap.add_argument("--compose-ahead", type=int, default=1, choices=(0, 1),
                     help="1: after each step compose the runs of partitions the next step "
                          "reuses into groups (dita_state_cache_compose_runs); timed")
+    ap.add_argument("--planner", choices=("fixed", "error"), default="fixed",
+                    help="trajectory only: the workload's fixed schedule, or the error-guided "
+                         "group planner (dita_planner_*) fed by the statistics kernels")
+    ap.add_argument("--budget", type=float, default=0.004,
+                    help="error planner: estimated error allowed to be reused per step")
+    ap.add_argument("--group-size", type=int, default=2, help="error planner: partitions per group")
+    ap.add_argument("--fresh-weight", type=float, default=0.0,
+                    help="error planner: groups holding a partition of at least this "
+                         "contribution are always computed (0: off)")
+    ap.add_argument("--planner-anchor", type=int, default=0,
+                    help="error planner: anchor period (0: only the cold step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the library's state-copy kernel over BYTES of O (the "
                          "reference point for HBM byte counters) and exit")
@@ -258,7 +269,7 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
     }
 
 
-def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False):
+def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None):
     """The schedule once from a cold cache beside an all-fresh reference (same library,
     same K/V, every partition recomputed): per-step error of the reused output, fresh
     blocks, step latency, and the contribution profile by partition distance."""
@@ -277,15 +288,38 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False):
     all_fresh = np.zeros(wl.P, dtype=np.uint8)
     out = {"fresh": [], "step_ms": [], "err_max_abs": [], "err_rel_fro": [], "lse_err_max_abs": []}
     contribution = None
+    planner = None
+    if eplan is not None:
+        # error-guided planner: weights from the contribution kernel on all-fresh
+        # steps, the local state's change measured after every step
+        planner = dita.ErrorPlanner(wl.P, wl.q_part, eplan["group_size"], eplan["budget"],
+                                    eplan["anchor_period"], eplan["fresh_weight"])
+        prev_o = torch.zeros(shape, dtype=tdt, device=dev)
+        prev_l = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        chg = torch.zeros(3, dtype=torch.float64, device=dev)
+        out["planner"] = dict(eplan, est_err_reused=[], local_change=[])
     for s in range(wl.steps):
         k, v = inp.kv(s)
         ks, vs = upload_parts(k, wl, dev, tdt), upload_parts(v, wl, dev, tdt)
         del k, v
-        mask = dita.dita_plan_mask(plan, s, cache)
+        if planner is None:
+            mask = dita.dita_plan_mask(plan, s, cache)
+        else:
+            mask, est = planner.mask(s, cache=cache)
+            out["planner"]["est_err_reused"].append(float(est[mask == 1].sum()))
         ev = (dita.Event(), dita.Event(), dita.Event())
         _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, s, o=o, lse=lse, stream=stream,
                                          events=(ev[0].handle, ev[1].handle, ev[2].handle))
-        if compose_ahead and s + 1 < wl.steps:
+        if planner is not None:
+            if info.n_fresh == wl.P:
+                planner.set_weights(list(cache.contrib(lse, stream=stream).cpu().numpy()))
+            so, sl = cache.slot(wl.q_part)
+            dita.dita_state_change(so, prev_o, sl, prev_l, roll=True, out=chg, stream=stream)
+            if s > 0:
+                d = float(chg[2].item())
+                planner.observe(s, d)
+                out["planner"]["local_change"].append(d)
+        elif compose_ahead and s + 1 < wl.steps:
             cache.compose_runs(dita.dita_plan_mask(plan, s + 1, cache), stream=stream)
         dita.dita_attn_step(ref, q, ks, vs, all_fresh, s, o=o_ref, lse=lse_ref, stream=stream)
         torch.cuda.synchronize()
@@ -475,8 +509,12 @@ def main():
         del kv, cache
         torch.cuda.empty_cache()
         log("[bench] trajectory: the schedule from a cold cache beside an all-fresh reference")
+        eplan = None
+        if args.planner == "error":
+            eplan = {"group_size": args.group_size, "budget": args.budget,
+                     "anchor_period": args.planner_anchor, "fresh_weight": args.fresh_weight}
         result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream,
-                                          compose_ahead=bool(args.compose_ahead))
+                                          compose_ahead=bool(args.compose_ahead), eplan=eplan)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)

@@ -370,7 +370,9 @@ int dita_state_change(const dita_shape* shape, const void* o_new, const float* l
  * All partitions are fresh on an anchor step (anchor_period > 0 and
  * step % anchor_period == 0), before weights are set, and before a change
  * observed at a step < `step` exists; the local partition is always fresh; a
- * group with an invalid slot is fresh.  Sums run in ascending index order.
+ * group with an invalid slot is fresh, and so is (fresh_weight > 0) a group
+ * holding a partition whose weight is >= fresh_weight (the page: high-
+ * contribution partitions are computed).  Sums run in ascending index order.
  */
 typedef struct {
   int32_t P;              /* partitions, 1..DITA_MAX_PARTITIONS                */
@@ -378,6 +380,7 @@ typedef struct {
   int32_t group_size;     /* partitions per group, >= 1                        */
   int32_t anchor_period;  /* > 0: every anchor_period-th step is all fresh     */
   double budget;          /* total estimated error allowed to be reused, >= 0  */
+  double fresh_weight;    /* > 0: groups with a weight >= this are always fresh */
 } dita_error_plan;
 
 typedef struct dita_planner dita_planner;

@@ -34,7 +34,10 @@ Readings taken here (the plainest ones the page supports):
   ``budget``; every other group is computed;
 * forced fresh: the local partition; every partition on an anchor step, when
   no weights are set yet, or when no change has been observed yet; every
-  member of a group holding a slot without a state.
+  member of a group holding a slot without a state; and, when
+  ``fresh_weight`` > 0, every member of a group holding a partition whose
+  weight is at least ``fresh_weight`` (the page: high-contribution partitions
+  are computed).
 """
 
 from __future__ import annotations
@@ -75,13 +78,15 @@ def state_change(o_new, o_prev) -> float:
 class ErrorPlanner:
     """Group-wise, error-budgeted compute-or-reuse planner (readings above)."""
 
-    def __init__(self, P: int, q: int, group_size: int, budget: float, anchor_period: int = 0):
+    def __init__(self, P: int, q: int, group_size: int, budget: float, anchor_period: int = 0,
+                 fresh_weight: float = 0.0):
         if not (1 <= P <= 64 and 0 <= q < P and group_size >= 1 and budget >= 0.0
-                and anchor_period >= 0):
+                and anchor_period >= 0 and fresh_weight >= 0.0):
             raise ValueError("bad planner parameters")
         self.P, self.q, self.g = P, q, group_size
         self.budget = float(budget)
         self.anchor_period = anchor_period
+        self.fresh_weight = float(fresh_weight)
         self.weights: Optional[List[float]] = None
         self.delta: Dict[int, float] = {}
 
@@ -125,6 +130,8 @@ class ErrorPlanner:
         for j, (a, b) in enumerate(self.groups()):
             members = [p for p in range(a, b + 1) if p != q]
             if not members or not all(valid[p] for p in members):
+                continue
+            if self.fresh_weight > 0.0 and any(self.weights[p] >= self.fresh_weight for p in members):
                 continue
             e = 0.0
             for p in members:

@@ -66,7 +66,8 @@ class StepInfo(ctypes.Structure):
 
 class ErrorPlan(ctypes.Structure):
     _fields_ = [("P", ctypes.c_int32), ("q", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("anchor_period", ctypes.c_int32), ("budget", ctypes.c_double)]
+                ("anchor_period", ctypes.c_int32), ("budget", ctypes.c_double),
+                ("fresh_weight", ctypes.c_double)]
 
 
 class StepOpts(ctypes.Structure):
@@ -457,11 +458,13 @@ def dita_state_change(o_new, o_prev, lse_new=None, lse_prev=None, roll: bool = F
 class ErrorPlanner:
     """The library's error-guided, group-wise planner (dita_planner_*)."""
 
-    def __init__(self, P: int, q: int, group_size: int, budget: float, anchor_period: int = 0):
+    def __init__(self, P: int, q: int, group_size: int, budget: float, anchor_period: int = 0,
+                 fresh_weight: float = 0.0):
         self.P = P
         h = ctypes.c_void_p()
         _check(_lib.dita_planner_create(ctypes.byref(h), ctypes.byref(
-            ErrorPlan(P, q, group_size, anchor_period, float(budget)))), "dita_planner_create")
+            ErrorPlan(P, q, group_size, anchor_period, float(budget), float(fresh_weight)))),
+            "dita_planner_create")
         self.handle = h.value
 
     def set_weights(self, w: Sequence[float]):

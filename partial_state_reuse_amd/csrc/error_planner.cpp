@@ -18,7 +18,8 @@
 //            running error stays within the budget; the rest are computed.
 // Everything is fresh on an anchor step, before weights are set and before a
 // change has been observed; the local partition is always fresh; a group
-// holding an invalid slot is fresh.  All sums run in ascending index order in
+// holding an invalid slot, or (fresh_weight > 0) a partition of weight >=
+// fresh_weight, is fresh.  All sums run in ascending index order in
 // float64, so an implementation that follows the same order agrees bit for bit.
 
 #include <algorithm>
@@ -42,7 +43,8 @@ namespace {
 
 bool error_plan_valid(const dita_error_plan& p) {
   return p.P >= 1 && p.P <= DITA_MAX_PARTITIONS && p.q >= 0 && p.q < p.P && p.group_size >= 1 &&
-         p.anchor_period >= 0 && !std::isnan(p.budget) && p.budget >= 0.0;
+         p.anchor_period >= 0 && !std::isnan(p.budget) && p.budget >= 0.0 &&
+         !std::isnan(p.fresh_weight) && p.fresh_weight >= 0.0;
 }
 
 // delta~_t for planning `step`: observations after step - 1 are not known yet.
@@ -86,6 +88,7 @@ void error_plan_mask(const dita_planner& pl, int64_t step, const uint8_t* valid,
       if (p == q) continue;
       any = true;
       ok = ok && valid[p];
+      if (pl.plan.fresh_weight > 0.0 && pl.w[p] >= pl.plan.fresh_weight) ok = false;
       e += err[p];
     }
     if (any && ok) cands.push_back({e, j});

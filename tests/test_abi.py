@@ -281,8 +281,9 @@ def test_error_planner_matches_oracle_bit_for_bit():
         g = int(rng.integers(1, 6))
         ap = int(rng.choice([0, 0, 3, 5, 7]))
         budget = float(rng.choice([0.0, rng.uniform(0, 0.02), rng.uniform(0, 0.2), np.inf]))
-        ref = OracleErrorPlanner(P, q, g, budget, ap)
-        lib_pl = dita.ErrorPlanner(P, q, g, budget, ap)
+        fw = float(rng.choice([0.0, 0.0, rng.uniform(0.02, 0.2)]))
+        ref = OracleErrorPlanner(P, q, g, budget, ap, fw)
+        lib_pl = dita.ErrorPlanner(P, q, g, budget, ap, fw)
         if rng.random() < 0.95:
             w = rng.dirichlet(np.ones(P) * 0.5)
             ref.set_weights(list(w))
@@ -304,12 +305,13 @@ def test_error_planner_matches_oracle_bit_for_bit():
 
 
 def test_error_planner_validation():
-    bad = [(0, 0, 1, 0, 0.1), (4, 4, 1, 0, 0.1), (4, 0, 0, 0, 0.1), (4, 0, 1, -1, 0.1),
-           (4, 0, 1, 0, -0.5), (4, 0, 1, 0, float("nan"))]
+    bad = [(0, 0, 1, 0, 0.1, 0.0), (4, 4, 1, 0, 0.1, 0.0), (4, 0, 0, 0, 0.1, 0.0),
+           (4, 0, 1, -1, 0.1, 0.0), (4, 0, 1, 0, -0.5, 0.0), (4, 0, 1, 0, float("nan"), 0.0),
+           (4, 0, 1, 0, 0.1, -0.2), (4, 0, 1, 0, 0.1, float("nan"))]
     h = ctypes.c_void_p()
-    for P, q, g, ap, b in bad:
-        assert lib.dita_planner_create(ctypes.byref(h), ctypes.byref(dita.ErrorPlan(P, q, g, ap, b))) == dita.DITA_ERR_ARG
-    assert lib.dita_planner_create(None, ctypes.byref(dita.ErrorPlan(4, 0, 1, 0, 0.1))) == dita.DITA_ERR_ARG
+    for args in bad:
+        assert lib.dita_planner_create(ctypes.byref(h), ctypes.byref(dita.ErrorPlan(*args))) == dita.DITA_ERR_ARG
+    assert lib.dita_planner_create(None, ctypes.byref(dita.ErrorPlan(4, 0, 1, 0, 0.1, 0.0))) == dita.DITA_ERR_ARG
     pl = dita.ErrorPlanner(4, 0, 2, 0.1)
     dbl = lambda *x: (ctypes.c_double * 4)(*x)
     assert lib.dita_planner_set_weights(pl.handle, dbl(0.1, -0.1, 0.5, 0.5)) == dita.DITA_ERR_ARG

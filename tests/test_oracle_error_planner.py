@@ -173,3 +173,20 @@ def test_bad_parameters():
     for step, d in ((-1, 0.1), (2, -0.1), (2, math.inf), (2, math.nan)):
         with pytest.raises(ValueError):
             pl.observe(step, d)
+
+
+def test_high_contribution_groups_are_computed():
+    """With fresh_weight set, a group holding a partition of at least that weight is
+    never reused, whatever the budget; the hand-worked case with fresh_weight 0.2
+    keeps group {1} (weight 0.2) fresh and reuses the others within the budget."""
+    pl = _planner()
+    pl.fresh_weight = 0.2
+    pl.budget = 1.0
+    valid, stamp = [1] * 6, [2, 0, 0, 1, 0, 0]
+    assert list(pl.mask(3, valid, stamp)[0]) == [0, 0, 1, 1, 1, 1]
+    pl.fresh_weight = 0.15          # {2,3} holds weights 0.15 too
+    assert list(pl.mask(3, valid, stamp)[0]) == [0, 0, 0, 0, 1, 1]
+    pl.fresh_weight = 0.5           # nobody but the local partition reaches it
+    assert list(pl.mask(3, valid, stamp)[0]) == [0, 1, 1, 1, 1, 1]
+    with pytest.raises(ValueError):
+        ErrorPlanner(P=4, q=0, group_size=1, budget=0.1, fresh_weight=-0.1)

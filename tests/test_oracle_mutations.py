@@ -101,6 +101,9 @@ MUTATIONS = [
      "members = [p for p in range(a, b + 1) if p != q]", "members = [p for p in range(a, b + 1)]"),
     ("error_planner.py", "groups taken in decreasing error",
      "candidates.sort(key=lambda c: (c[0], c[1]))", "candidates.sort(key=lambda c: (-c[0], c[1]))"),
+    ("error_planner.py", "high-contribution threshold exclusive",
+     "any(self.weights[p] >= self.fresh_weight for p in members)",
+     "any(self.weights[p] > self.fresh_weight for p in members)"),
     ("error_planner.py", "error without the weight", "err[p] = self.weights[p] * growth",
      "err[p] = growth"),
     ("planner.py", "SplitMix64 multiplier typo", "0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
