@@ -151,14 +151,50 @@ typedef struct dita_state_cache dita_state_cache;
 /* Device bytes a cache of P slots needs; 0 if the shape or P is invalid. */
 size_t dita_state_cache_bytes(const dita_shape* shape, int P);
 
-/* Create a handle over `dev_buf`; all slots start invalid.  *out is set only on DITA_OK. */
+/* Create a handle over `dev_buf`; all slots start invalid.  *out is set only on DITA_OK.
+ * Partition p owns physical slot p for the handle's lifetime. */
 int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
                           size_t bytes);
+
+/*
+ * A pooled cache: P partitions share S <= P physical slots (bytes >=
+ * dita_state_cache_bytes(shape, S)).  A partition holds a slot only while its
+ * own state is on the device; composing a group, moving a state to the host,
+ * or invalidating it returns the slot to the pool, and storing, computing or
+ * fetching a state takes the lowest free one (DITA_ERR_SIZE, before any
+ * launch, when none is free).  Page section: State-Centric Parallel Runtime >
+ * Dynamic Group Compose (composition relieves memory pressure) -- with a pool,
+ * the states a cache no longer holds are device memory the next state can use.
+ */
+int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, int P, int S,
+                               void* dev_buf, size_t bytes);
+
+/*
+ * Move group leader p's state to caller host memory (pinned memory --
+ * hipHostMalloc -- lets the copies overlap other work): host_o holds
+ * B*H*Nq*D elements of the dtype, host_lse B*H*Nq floats; both must stay
+ * allocated, and must not be written, until the state is fetched, stored over
+ * or invalidated.  Stream-ordered device-to-host copies; in a pooled cache the
+ * slot returns to the pool.  The state stays valid: a step that reuses it, or
+ * dita_state_cache_fetch, copies it back.  Page section: State-Centric
+ * Parallel Runtime > Pipeline Orchestration ("reuse" operations load cached
+ * states).  DITA_ERR_STATE unless p leads a valid group held on the device.
+ */
+int dita_state_cache_offload(dita_state_cache* cache, int p, void* host_o, float* host_lse,
+                             void* stream);
+
+/* Copy an offloaded state back into a device slot (DITA_ERR_SIZE if none is free). */
+int dita_state_cache_fetch(dita_state_cache* cache, int p, void* stream);
+
+/* Valid states (group leaders) on the device and on the host, and physical slots not holding one. */
+int dita_state_cache_residency(const dita_state_cache* cache, int* on_device, int* on_host,
+                               int* free_slots);
 
 /* Destroy a handle (NULL is accepted).  Never frees dev_buf. */
 int dita_state_cache_free(dita_state_cache* cache);
 
-/* Device addresses of slot p's O and LSE (either output pointer may be NULL). */
+/* Device addresses of partition p's slot (either output pointer may be NULL).
+ * DITA_ERR_STATE in a pooled cache when p holds no slot. */
 int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse);
 
 /* Copy a state into slot p (stream-ordered copy kernel) and mark it valid with `step`.
@@ -291,6 +327,8 @@ typedef struct {
   int32_t merge_sources;    /* [out] states read by the final merge on `stream`         */
   int32_t premerge_sources; /* [out] reused states pre-merged on the side stream, or 0  */
   double premerge_bytes;    /* [out] (premerge_sources + 1) * bytes of one state, or 0  */
+  int32_t fetched;          /* [out] reused states copied back from host memory         */
+  int32_t reserved_out;     /* [out] 0                                                  */
 } dita_step_info;
 
 int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
@@ -302,6 +340,8 @@ int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_
  * critical path.  Page section: State-Centric Parallel Runtime > Pipeline
  * Orchestration (reuse operations fill the bubbles of the compute pipeline).
  *
+ * Reused states that were moved to host memory are copied back first (on the
+ * side stream when one is given, so the copies overlap the fresh attention).
  * When opts->side_stream is non-NULL and differs from `stream`, at least one
  * partition is fresh and at least max(2, opts->min_premerge) group states are
  * reused, the reused states are merged into (o, lse) on the side stream while

@@ -61,7 +61,8 @@ class StepInfo(ctypes.Structure):
                 ("fresh_flops", ctypes.c_double), ("merge_bytes", ctypes.c_double),
                 ("ev_begin", ctypes.c_void_p), ("ev_attn_end", ctypes.c_void_p),
                 ("ev_end", ctypes.c_void_p), ("merge_sources", ctypes.c_int32),
-                ("premerge_sources", ctypes.c_int32), ("premerge_bytes", ctypes.c_double)]
+                ("premerge_sources", ctypes.c_int32), ("premerge_bytes", ctypes.c_double),
+                ("fetched", ctypes.c_int32), ("reserved_out", ctypes.c_int32)]
 
 
 class ErrorPlan(ctypes.Structure):
@@ -94,6 +95,11 @@ def _load() -> ctypes.CDLL:
         "dita_state_merge": (i32, [ctypes.POINTER(Shape), i32, pvp, pvp, vp, vp, vp]),
         "dita_state_cache_bytes": (sz, [ctypes.POINTER(Shape), i32]),
         "dita_state_cache_init": (i32, [pvp, ctypes.POINTER(Shape), i32, vp, sz]),
+        "dita_state_cache_init_pool": (i32, [pvp, ctypes.POINTER(Shape), i32, i32, vp, sz]),
+        "dita_state_cache_offload": (i32, [vp, i32, vp, vp, vp]),
+        "dita_state_cache_fetch": (i32, [vp, i32, vp]),
+        "dita_state_cache_residency": (i32, [vp, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                             ctypes.POINTER(ctypes.c_int)]),
         "dita_state_cache_free": (i32, [vp]),
         "dita_state_cache_slot": (i32, [vp, i32, pvp, pvp]),
         "dita_state_cache_store": (i32, [vp, i32, vp, vp, i64, vp]),
@@ -256,11 +262,13 @@ class StateCache:
     """Device-resident (O_p, LSE_p) slots (the dita_state_cache_* calls).
 
     The device buffer is a torch uint8 tensor owned by this object; the C
-    handle only records its address.
+    handle only records its address.  ``slots`` < P makes a pooled cache of that
+    many physical slots (dita_state_cache_init_pool).  Host buffers of offloaded
+    states are pinned tensors kept alive here until the state comes back.
     """
 
     def __init__(self, B: int, H: int, Nq: int, D: int, dtype, P: int, device="cuda",
-                 scale: float = 0.0):
+                 scale: float = 0.0, slots: Optional[int] = None):
         torch = _torch()
         code = DITA_BF16 if dtype == torch.bfloat16 else DITA_F32 if dtype == torch.float32 else None
         if code is None:
@@ -268,15 +276,21 @@ class StateCache:
         self.shape = Shape(B, H, D, code, Nq, float(scale))
         self.P = P
         self.dtype = dtype
-        nbytes = _lib.dita_state_cache_bytes(ctypes.byref(self.shape), P)
+        self.slots = P if slots is None else int(slots)
+        nbytes = _lib.dita_state_cache_bytes(ctypes.byref(self.shape), self.slots)
         if nbytes == 0:
-            raise ValueError("invalid cache shape or P")
+            raise ValueError("invalid cache shape or slot count")
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
         h = ctypes.c_void_p()
-        _check(_lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(self.shape), P,
-                                          self.buffer.data_ptr(), nbytes), "dita_state_cache_init")
+        if slots is None:
+            _check(_lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(self.shape), P,
+                                              self.buffer.data_ptr(), nbytes), "dita_state_cache_init")
+        else:
+            _check(_lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(self.shape), P,
+                                                   self.slots, self.buffer.data_ptr(), nbytes),
+                   "dita_state_cache_init_pool")
         self.handle = h.value
-        self._views = [self._slot_views(p) for p in range(P)]
+        self._host = {}
 
     def _slot_views(self, p: int):
         torch = _torch()
@@ -293,8 +307,30 @@ class StateCache:
                 lse.view(torch.float32).view(s.B, s.H, s.Nq))
 
     def slot(self, p: int):
-        """Views (O_p, LSE_p) of slot p's device memory."""
-        return self._views[p]
+        """Views (O_p, LSE_p) of the device memory of partition p's slot."""
+        return self._slot_views(p)
+
+    def offload(self, p: int, stream=None):
+        """Move leader p's state to pinned host memory (copies on ``stream``)."""
+        torch = _torch()
+        s = self.shape
+        ho = torch.empty((s.B, s.H, s.Nq, s.D), dtype=self.dtype, pin_memory=True)
+        hl = torch.empty((s.B, s.H, s.Nq), dtype=torch.float32, pin_memory=True)
+        _check(_lib.dita_state_cache_offload(self.handle, p, ho.data_ptr(), hl.data_ptr(),
+                                             _stream(self.buffer, stream)), "dita_state_cache_offload")
+        self._host[p] = (ho, hl)
+        return ho, hl
+
+    def fetch(self, p: int, stream=None):
+        _check(_lib.dita_state_cache_fetch(self.handle, p, _stream(self.buffer, stream)),
+               "dita_state_cache_fetch")
+
+    def residency(self):
+        """(states on the device, states on the host, free physical slots)."""
+        a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(_lib.dita_state_cache_residency(self.handle, ctypes.byref(a), ctypes.byref(b),
+                                               ctypes.byref(c)), "dita_state_cache_residency")
+        return a.value, b.value, c.value
 
     def store(self, p: int, o, lse, step: int, stream=None):
         _check(_lib.dita_state_cache_store(self.handle, p, _ptr(o), _ptr(lse), step,

@@ -28,6 +28,12 @@ struct dita_state_cache {
   int16_t group[DITA_MAX_PARTITIONS];  // leader (first partition) of p's group
   hipEvent_t ev_fork;                  // stream -> side stream, created on first use
   hipEvent_t ev_join;                  // side stream -> stream
+  int S;                               // physical slots in the buffer
+  bool pool;                           // slots assigned on demand; else partition p owns slot p
+  int16_t phys[DITA_MAX_PARTITIONS];   // physical slot holding p's own state, -1 if none
+  uint8_t on_host[DITA_MAX_PARTITIONS];  // p's state lives in caller host memory
+  void* host_o[DITA_MAX_PARTITIONS];
+  float* host_lse[DITA_MAX_PARTITIONS];
 };
 
 namespace {
@@ -103,9 +109,41 @@ int check_slot(const dita_state_cache* c, int p) {
   return DITA_OK;
 }
 
-void* slot_o(const dita_state_cache* c, int p) { return c->base + size_t(p) * c->slot_stride; }
-float* slot_lse(const dita_state_cache* c, int p) {
-  return reinterpret_cast<float*>(c->base + size_t(p) * c->slot_stride + c->lse_offset);
+void* phys_o(const dita_state_cache* c, int k) { return c->base + size_t(k) * c->slot_stride; }
+float* phys_lse(const dita_state_cache* c, int k) {
+  return reinterpret_cast<float*>(c->base + size_t(k) * c->slot_stride + c->lse_offset);
+}
+// Device state of partition p (its physical slot must be assigned).
+void* slot_o(const dita_state_cache* c, int p) { return phys_o(c, c->phys[p]); }
+float* slot_lse(const dita_state_cache* c, int p) { return phys_lse(c, c->phys[p]); }
+
+// A state that is valid, leads its group and sits in device memory.
+bool resident(const dita_state_cache* c, int p) {
+  return c->valid[p] && c->group[p] == p && c->phys[p] >= 0 && !c->on_host[p];
+}
+
+// Lowest physical slot that no partition holds and `taken` does not mark; marks it.
+int take_free(const dita_state_cache* c, uint64_t* taken) {
+  uint64_t used = *taken;
+  for (int p = 0; p < c->P; ++p)
+    if (c->phys[p] >= 0) used |= uint64_t(1) << c->phys[p];
+  for (int k = 0; k < c->S; ++k)
+    if (!((used >> k) & 1)) {
+      *taken |= uint64_t(1) << k;
+      return k;
+    }
+  return -1;
+}
+
+// In a pooled cache a partition without a state of its own holds no slot.
+void release(dita_state_cache* c, int p) {
+  if (c->pool) c->phys[p] = -1;
+}
+
+void forget_host(dita_state_cache* c, int p) {
+  c->on_host[p] = 0;
+  c->host_o[p] = nullptr;
+  c->host_lse[p] = nullptr;
 }
 
 // Last partition of the group led by `first`.
@@ -119,6 +157,8 @@ void reset_slot(dita_state_cache* c, int p) {
   c->valid[p] = 0;
   c->stamp[p] = -1;
   c->group[p] = int16_t(p);
+  forget_host(c, p);
+  release(c, p);
 }
 
 // The mask a step applies: a group of two or more is reused only when every
@@ -166,6 +206,7 @@ int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, 
     c->group[p] = int16_t(first);
     c->valid[p] = 1;
     c->stamp[p] = oldest;
+    if (p != first) release(c, p);
   }
   if (launched) *launched = n > 1 ? 1 : 0;
   return DITA_OK;
@@ -241,29 +282,52 @@ size_t dita_state_cache_bytes(const dita_shape* shape, int P) {
   return size_t(P) * (align256(state_o_bytes(*shape)) + align256(state_lse_bytes(*shape)));
 }
 
-int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
-                          size_t bytes) {
+}  // extern "C"
+
+namespace {
+
+int cache_init(dita_state_cache** out, const dita_shape* shape, int P, int S, bool pool,
+               void* dev_buf, size_t bytes) {
   if (!out) return DITA_ERR_ARG;
   int st = check_shape(shape);
   if (st) return st;
-  if (P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if (P < 1 || P > DITA_MAX_PARTITIONS || S < 1 || S > P) return DITA_ERR_SHAPE;
   if ((st = check_dev(dev_buf))) return st;
-  const size_t need = dita_state_cache_bytes(shape, P);
+  const size_t need = dita_state_cache_bytes(shape, S);
   if (bytes < need) return DITA_ERR_SIZE;
   dita_state_cache* c = new (std::nothrow) dita_state_cache;
   if (!c) return DITA_ERR_ARG;
   c->shape = *shape;
   c->P = P;
+  c->S = S;
+  c->pool = pool;
   c->base = static_cast<char*>(dev_buf);
   c->bytes = bytes;
   c->o_bytes = state_o_bytes(*shape);
   c->lse_offset = align256(c->o_bytes);
   c->slot_stride = c->lse_offset + align256(state_lse_bytes(*shape));
-  for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) reset_slot(c, p);
+  for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) {
+    c->phys[p] = int16_t(pool || p >= P ? -1 : p);
+    reset_slot(c, p);
+  }
   c->ev_fork = nullptr;
   c->ev_join = nullptr;
   *out = c;
   return DITA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
+                          size_t bytes) {
+  return cache_init(out, shape, P, P, false, dev_buf, bytes);
+}
+
+int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, int P, int S,
+                               void* dev_buf, size_t bytes) {
+  return cache_init(out, shape, P, S, true, dev_buf, bytes);
 }
 
 int dita_state_cache_free(dita_state_cache* cache) {
@@ -281,6 +345,7 @@ int dita_state_cache_free(dita_state_cache* cache) {
 int dita_state_cache_slot(const dita_state_cache* cache, int p, void** o, float** lse) {
   const int st = check_slot(cache, p);
   if (st) return st;
+  if (cache->phys[p] < 0) return DITA_ERR_STATE;
   if (o) *o = slot_o(cache, p);
   if (lse) *lse = slot_lse(cache, p);
   return DITA_OK;
@@ -297,9 +362,14 @@ int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const 
   if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
       overlaps(lse, lb, cache->base, cache->bytes))
     return DITA_ERR_ARG;
-  st = hip_status(dita::launch_copy_state(o, lse, slot_o(cache, p), slot_lse(cache, p),
+  uint64_t taken = 0;
+  const int k = cache->phys[p] >= 0 ? cache->phys[p] : take_free(cache, &taken);
+  if (k < 0) return DITA_ERR_SIZE;
+  st = hip_status(dita::launch_copy_state(o, lse, phys_o(cache, k), phys_lse(cache, k),
                                           cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
   if (st) return st;
+  cache->phys[p] = int16_t(k);
+  forget_host(cache, p);
   cache->valid[p] = 1;
   cache->stamp[p] = step;
   return DITA_OK;
@@ -314,6 +384,12 @@ int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* 
   if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
       overlaps(lse, lb, cache->base, cache->bytes))
     return DITA_ERR_ARG;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (cache->on_host[p]) {
+    if ((st = hip_status(hipMemcpyAsync(o, cache->host_o[p], cache->o_bytes, hipMemcpyHostToDevice, hs))))
+      return st;
+    return hip_status(hipMemcpyAsync(lse, cache->host_lse[p], lb, hipMemcpyHostToDevice, hs));
+  }
   return hip_status(dita::launch_copy_state(slot_o(cache, p), slot_lse(cache, p), o, lse,
                                             cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
 }
@@ -353,6 +429,8 @@ int dita_state_cache_compose(dita_state_cache* cache, int first, int last, void*
     if (!cache->valid[p]) return DITA_ERR_STATE;
     if (cache->group[p] < first || group_last(cache, cache->group[p]) > last) return DITA_ERR_ARG;
   }
+  for (int p = first; p <= last; ++p)
+    if (cache->group[p] == p && !resident(cache, p)) return DITA_ERR_STATE;  // fetch it first
   return compose_range(cache, first, last, static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -381,6 +459,9 @@ int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse,
       ++n;
     }
   }
+  for (int i = 0; i < n; ++i)
+    for (int p = first[i]; p <= last[i]; ++p)
+      if (cache->group[p] == p && !resident(cache, p)) return DITA_ERR_STATE;  // fetch it first
   int launched = 0;
   for (int i = 0; i < n; ++i) {
     int l = 0;
@@ -452,6 +533,11 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
 
   uint8_t reuse[DITA_MAX_PARTITIONS];
   if ((st = effective_mask(cache, reuse_mask, reuse))) return st;
+  // Physical slots: fresh partitions without one, and reused states that sit in
+  // host memory (fetched back before the merge), take free slots.
+  int16_t phys[DITA_MAX_PARTITIONS];
+  uint64_t taken = 0;
+  for (int p = 0; p < P; ++p) phys[p] = cache->phys[p];
   dita::AttnJobs jobs;
   int n_fresh = 0;
   double fresh_keys = 0.0;
@@ -459,55 +545,85 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     if (reuse[p]) continue;
     if ((st = check_dev(k_list[p])) || (st = check_dev(v_list[p]))) return st;
     if (!nk_ok(s, nk_list[p])) return DITA_ERR_SHAPE;
-    jobs.job[n_fresh++] = dita::AttnJob{k_list[p], v_list[p], slot_o(cache, p), slot_lse(cache, p),
-                                        nk_list[p]};
+    if (phys[p] < 0 && (phys[p] = int16_t(take_free(cache, &taken))) < 0) return DITA_ERR_SIZE;
+    jobs.job[n_fresh++] =
+        dita::AttnJob{k_list[p], v_list[p], phys_o(cache, phys[p]), phys_lse(cache, phys[p]), nk_list[p]};
     fresh_keys += double(nk_list[p]);
   }
-  // Reused group states (leaders) and fresh states, in partition order.
+  // Reused group states (leaders), in partition order; those on the host are fetched.
   int reused_heads[DITA_MAX_PARTITIONS], n_reused_heads = 0;
-  for (int p = 0; p < P; ++p)
-    if (reuse[p] && cache->group[p] == p) reused_heads[n_reused_heads++] = p;
+  int fetch[DITA_MAX_PARTITIONS], n_fetch = 0;
+  for (int p = 0; p < P; ++p) {
+    if (!reuse[p] || cache->group[p] != p) continue;
+    reused_heads[n_reused_heads++] = p;
+    if (cache->on_host[p]) {
+      if (phys[p] < 0 && (phys[p] = int16_t(take_free(cache, &taken))) < 0) return DITA_ERR_SIZE;
+      fetch[n_fetch++] = p;
+    }
+  }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipStream_t side = opts ? static_cast<hipStream_t>(opts->side_stream) : nullptr;
+  if (side == hs) side = nullptr;
   const int min_pre = opts && opts->min_premerge > 2 ? opts->min_premerge : 2;
-  const bool premerge = side && side != hs && n_fresh > 0 && n_reused_heads >= min_pre;
-  if (premerge && (st = ensure_events(cache))) return st;
+  const bool premerge = side && n_fresh > 0 && n_reused_heads >= min_pre;
+  const bool use_side = side && (premerge || n_fetch > 0);
+  if (use_side && (st = ensure_events(cache))) return st;
 
   if (info && info->ev_begin && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_begin), hs))))
     return st;
   const int64_t rows = int64_t(s.B) * s.H * s.Nq;
-  if (premerge) {
+  hipStream_t aux = use_side ? side : hs;
+  if (use_side) {
     // The side stream starts after everything already on `stream` (earlier
-    // writers of the reused slots and users of o/lse) and merges the reused
-    // states into (o, lse) while the fresh attention runs.
-    dita::MergeSrc pre;
-    for (int i = 0; i < n_reused_heads; ++i) {
-      pre.o[i] = slot_o(cache, reused_heads[i]);
-      pre.lse[i] = slot_lse(cache, reused_heads[i]);
-    }
+    // writers of the reused slots and of the host copies, users of o/lse).
     if ((st = hip_status(hipEventRecord(cache->ev_fork, hs))) ||
-        (st = hip_status(hipStreamWaitEvent(side, cache->ev_fork, 0))) ||
-        (st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_reused_heads, pre, o, lse, side))) ||
-        (st = hip_status(hipEventRecord(cache->ev_join, side))))
+        (st = hip_status(hipStreamWaitEvent(side, cache->ev_fork, 0))))
       return st;
   }
+  for (int i = 0; i < n_fetch; ++i) {
+    const int p = fetch[i];
+    if ((st = hip_status(hipMemcpyAsync(phys_o(cache, phys[p]), cache->host_o[p], ob,
+                                        hipMemcpyHostToDevice, aux))) ||
+        (st = hip_status(hipMemcpyAsync(phys_lse(cache, phys[p]), cache->host_lse[p], lb,
+                                        hipMemcpyHostToDevice, aux))))
+      return st;
+  }
+  if (premerge) {
+    // Merge the reused states into (o, lse) while the fresh attention runs.
+    dita::MergeSrc pre;
+    for (int i = 0; i < n_reused_heads; ++i) {
+      pre.o[i] = phys_o(cache, phys[reused_heads[i]]);
+      pre.lse[i] = phys_lse(cache, phys[reused_heads[i]]);
+    }
+    if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_reused_heads, pre, o, lse, side))))
+      return st;
+  }
+  if (use_side && (st = hip_status(hipEventRecord(cache->ev_join, side)))) return st;
   if (n_fresh > 0 && (st = hip_status(launch_attn(s, q, jobs, n_fresh, hs)))) return st;
   if (info && info->ev_attn_end &&
       (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_attn_end), hs))))
     return st;
-  // Recomputed groups dissolve; fresh slots take this step's stamp.
-  for (int p = 0; p < P; ++p)
+  // Recomputed groups dissolve; fresh slots take this step's stamp; fetched
+  // states are resident again.
+  for (int p = 0; p < P; ++p) {
     if (!reuse[p]) {
       cache->valid[p] = 1;
       cache->stamp[p] = step;
       cache->group[p] = int16_t(p);
+      cache->phys[p] = phys[p];
+      forget_host(cache, p);
     }
+  }
+  for (int i = 0; i < n_fetch; ++i) {
+    cache->phys[fetch[i]] = phys[fetch[i]];
+    forget_host(cache, fetch[i]);
+  }
 
   dita::MergeSrc src;
   int n_src = 0;
+  if (use_side && (st = hip_status(hipStreamWaitEvent(hs, cache->ev_join, 0)))) return st;
   if (premerge) {
-    if ((st = hip_status(hipStreamWaitEvent(hs, cache->ev_join, 0)))) return st;
     src.o[n_src] = o;  // the pre-merged reused states; the merge writes it in place
     src.lse[n_src] = lse;
     ++n_src;
@@ -529,7 +645,63 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     info->merge_bytes = double(n_src + 1) * double(ob + lb);
     info->premerge_sources = premerge ? n_reused_heads : 0;
     info->premerge_bytes = premerge ? double(n_reused_heads + 1) * double(ob + lb) : 0.0;
+    info->fetched = n_fetch;
+    info->reserved_out = 0;
   }
+  return DITA_OK;
+}
+
+int dita_state_cache_offload(dita_state_cache* cache, int p, void* host_o, float* host_lse,
+                             void* stream) {
+  int st = check_slot(cache, p);
+  if (st) return st;
+  if (!host_o || !host_lse) return DITA_ERR_ARG;
+  if (!resident(cache, p)) return DITA_ERR_STATE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t lb = state_lse_bytes(cache->shape);
+  if ((st = hip_status(hipMemcpyAsync(host_o, slot_o(cache, p), cache->o_bytes,
+                                      hipMemcpyDeviceToHost, hs))) ||
+      (st = hip_status(hipMemcpyAsync(host_lse, slot_lse(cache, p), lb, hipMemcpyDeviceToHost, hs))))
+    return st;
+  cache->on_host[p] = 1;
+  cache->host_o[p] = host_o;
+  cache->host_lse[p] = host_lse;
+  release(cache, p);
+  return DITA_OK;
+}
+
+int dita_state_cache_fetch(dita_state_cache* cache, int p, void* stream) {
+  int st = check_slot(cache, p);
+  if (st) return st;
+  if (!cache->valid[p] || cache->group[p] != p || !cache->on_host[p]) return DITA_ERR_STATE;
+  uint64_t taken = 0;
+  const int k = cache->phys[p] >= 0 ? cache->phys[p] : take_free(cache, &taken);
+  if (k < 0) return DITA_ERR_SIZE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(hipMemcpyAsync(phys_o(cache, k), cache->host_o[p], cache->o_bytes,
+                                      hipMemcpyHostToDevice, hs))) ||
+      (st = hip_status(hipMemcpyAsync(phys_lse(cache, k), cache->host_lse[p],
+                                      state_lse_bytes(cache->shape), hipMemcpyHostToDevice, hs))))
+    return st;
+  cache->phys[p] = int16_t(k);
+  forget_host(cache, p);
+  return DITA_OK;
+}
+
+int dita_state_cache_residency(const dita_state_cache* cache, int* on_device, int* on_host,
+                               int* free_slots) {
+  if (!cache) return DITA_ERR_ARG;
+  int dev = 0, host = 0;
+  for (int p = 0; p < cache->P; ++p) {
+    if (!cache->valid[p] || cache->group[p] != p) continue;
+    if (cache->on_host[p])
+      ++host;
+    else
+      ++dev;
+  }
+  if (on_device) *on_device = dev;
+  if (on_host) *on_host = host;
+  if (free_slots) *free_slots = cache->S - dev;
   return DITA_OK;
 }
 
@@ -556,7 +728,7 @@ int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, do
   if ((st = check_dev(lse)) || (st = check_dev(w_out))) return st;
   const float* lses[DITA_MAX_PARTITIONS];
   for (int p = 0; p < cache->P; ++p) {
-    if (!cache->valid[p] || cache->group[p] != p || group_last(cache, p) != p) return DITA_ERR_STATE;
+    if (!resident(cache, p) || group_last(cache, p) != p) return DITA_ERR_STATE;
     lses[p] = slot_lse(cache, p);
   }
   return dita_state_contrib(&cache->shape, cache->P, lses, lse, w_out, stream);

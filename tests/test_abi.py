@@ -356,6 +356,38 @@ def test_stats_calls_validate_before_launch():
     lib.dita_state_cache_free(h)
 
 
+def test_pooled_cache_host_only():
+    """Pooled cache: sizes, slot lookup, and the slot shortage a step detects before
+    any launch; offload/fetch refuse states that do not exist."""
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    h = ctypes.c_void_p()
+    n2 = lib.dita_state_cache_bytes(ctypes.byref(shape), 2)
+    assert lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(shape), 4, 5, FAKE_DEV, n2 * 4) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(shape), 4, 0, FAKE_DEV, n2) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(shape), 4, 2, FAKE_DEV, n2 - 1) == dita.DITA_ERR_SIZE
+    assert lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(shape), 4, 2, FAKE_DEV, n2) == 0
+    hp = h.value
+    o, l = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.dita_state_cache_slot(hp, 0, ctypes.byref(o), ctypes.byref(l)) == dita.DITA_ERR_STATE
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.dita_state_cache_residency(hp, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
+    assert (a.value, b.value, c.value) == (0, 0, 2)
+    # four fresh partitions need four slots; the pool has two
+    base = FAKE_DEV + (64 << 20)
+    q, out, lse = base, base + (1 << 20), base + (2 << 20)
+    ks = (ctypes.c_void_p * 4)(*[base + ((3 + i) << 20) for i in range(4)])
+    nk = (ctypes.c_int64 * 4)(64, 64, 64, 64)
+    zeros = (ctypes.c_uint8 * 4)(0, 0, 0, 0)
+    assert lib.dita_attn_step(hp, q, ks, ks, nk, zeros, 0, out, lse, None, None) == dita.DITA_ERR_SIZE
+    host = base + (9 << 20)
+    assert lib.dita_state_cache_offload(hp, 0, host, host + 4096, None) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_offload(hp, 0, None, host, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_fetch(hp, 0, None) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_fetch(hp, 4, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_residency(None, None, None, None) == dita.DITA_ERR_ARG
+    lib.dita_state_cache_free(hp)
+
+
 def test_event_helpers_validate():
     assert lib.dita_event_create(None) == dita.DITA_ERR_ARG
     assert lib.dita_event_record(None, None) == dita.DITA_ERR_ARG
