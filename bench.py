@@ -269,6 +269,56 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
     }
 
 
+def offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan, reps: int = 3):
+    """A non-anchor step whose composed far group was moved to pinned host memory:
+    step time with the group resident, fetched on the step's stream, and fetched
+    on a side stream while the fresh attention runs (no pre-merge)."""
+    import torch
+    cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
+    o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
+    lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+    ks, vs = kv[0]
+    dita.dita_attn_step(cache, q, ks, vs, np.zeros(wl.P, np.uint8), 0, o=o, lse=lse, stream=stream)
+    mask = dita.dita_plan_mask(plan, 1, cache)
+    cache.compose_runs(mask, stream=stream)
+    groups = [p for p in cache.leaders() if cache.group(p)[1] > p]
+    if not groups or wl.dtype != "bf16":
+        return None
+    side = torch.cuda.Stream(device=dev)
+    ks1, vs1 = kv[1 % len(kv)]
+
+    def one(offload, side_stream):
+        if offload:
+            for p in groups:
+                cache.offload(p, stream=stream)
+        torch.cuda.synchronize()
+        b, e = dita.Event(), dita.Event()
+        b.record(stream)
+        _, _, info = dita.dita_attn_step(cache, q, ks1, vs1, mask, 1, o=o, lse=lse, stream=stream,
+                                         side_stream=side_stream, min_premerge=64)
+        e.record(stream)
+        ms = b.elapsed_ms(e)
+        assert info.fetched == (len(groups) if offload else 0)
+        return ms
+
+    res = {}
+    for name, off, ss in (("resident", False, None), ("fetch_on_stream", True, None),
+                          ("fetch_on_side_stream", True, side)):
+        one(off, ss)
+        res[name + "_ms"] = min(one(off, ss) for _ in range(reps))
+    fetched_bytes = len(groups) * wl.state_bytes()
+    res["fetched_bytes"] = fetched_bytes
+    extra = res["fetch_on_stream_ms"] - res["resident_ms"]
+    res["h2d_GBps_serial"] = fetched_bytes / (extra / 1e3) / 1e9 if extra > 0 else None
+    res["hidden_fraction"] = ((res["fetch_on_stream_ms"] - res["fetch_on_side_stream_ms"]) / extra
+                              if extra > 0 else None)
+    res["note"] = (f"{len(groups)} composed group state(s) in pinned host memory, copied back by "
+                   f"the step; fresh blocks {int((mask == 0).sum())}")
+    log(f"[bench] offload: resident {res['resident_ms']:.3f} ms, fetch on stream "
+        f"{res['fetch_on_stream_ms']:.3f} ms, on side stream {res['fetch_on_side_stream_ms']:.3f} ms")
+    return res
+
+
 def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None):
     """The schedule once from a cold cache beside an all-fresh reference (same library,
     same K/V, every partition recomputed): per-step error of the reused output, fresh
@@ -505,6 +555,8 @@ def main():
         },
     }
     result["isolated"] = isolated_bandwidth(dita, wl, tdt, dev, stream, q)
+    if wl.steps > 1 and n_res > 1:
+        result["offload"] = offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan)
     if args.trajectory:
         del kv, cache
         torch.cuda.empty_cache()
