@@ -294,6 +294,16 @@ int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t
                    uint8_t* reuse_out);
 
 /*
+ * The same mask as a 64-bit word: bit p set = partition p reused (bits >= P
+ * clear).  dita_mask_to_bits / dita_mask_from_bits convert between the two
+ * encodings (P in 1..DITA_MAX_PARTITIONS; mask bytes must be 0 or 1).
+ */
+int dita_plan_bits(const dita_plan* plan, const dita_state_cache* cache, int64_t step,
+                   uint64_t* reuse_bits);
+int dita_mask_to_bits(const uint8_t* mask, int P, uint64_t* bits);
+int dita_mask_from_bits(uint64_t bits, int P, uint8_t* mask);
+
+/*
  * dita_attn_step -- one rank-step of selective state reuse.
  * Page sections: 1. Anchor-Guided Selection Planner (per-partition compute or
  * reuse) and 2. State-Centric Parallel Runtime > State Composition.

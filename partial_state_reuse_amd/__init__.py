@@ -108,6 +108,9 @@ def _load() -> ctypes.CDLL:
         "dita_state_cache_info": (i32, [vp, i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(i64)]),
         "dita_state_cache_shape": (i32, [vp, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int)]),
         "dita_plan_mask": (i32, [ctypes.POINTER(Plan), vp, i64, ctypes.POINTER(ctypes.c_uint8)]),
+        "dita_plan_bits": (i32, [ctypes.POINTER(Plan), vp, i64, ctypes.POINTER(ctypes.c_uint64)]),
+        "dita_mask_to_bits": (i32, [ctypes.POINTER(ctypes.c_uint8), i32, ctypes.POINTER(ctypes.c_uint64)]),
+        "dita_mask_from_bits": (i32, [ctypes.c_uint64, i32, ctypes.POINTER(ctypes.c_uint8)]),
         "dita_state_cache_compose": (i32, [vp, i32, i32, vp]),
         "dita_state_cache_compose_runs": (i32, [vp, ctypes.POINTER(ctypes.c_uint8), vp,
                                                 ctypes.POINTER(ctypes.c_int)]),
@@ -256,6 +259,14 @@ def dita_plan_mask(plan: Plan, step: int, cache: Optional["StateCache"] = None) 
     _check(_lib.dita_plan_mask(ctypes.byref(plan), cache.handle if cache else None, step, out),
            "dita_plan_mask")
     return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+def dita_plan_bits(plan: Plan, step: int, cache: Optional["StateCache"] = None) -> int:
+    """The planner's mask as a 64-bit word (bit p set = reuse partition p)."""
+    out = ctypes.c_uint64()
+    _check(_lib.dita_plan_bits(ctypes.byref(plan), cache.handle if cache else None, step,
+                               ctypes.byref(out)), "dita_plan_bits")
+    return out.value
 
 
 class StateCache:

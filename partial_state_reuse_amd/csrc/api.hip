@@ -508,6 +508,33 @@ int dita_plan_mask(const dita_plan* plan, const dita_state_cache* cache, int64_t
   return DITA_OK;
 }
 
+int dita_mask_to_bits(const uint8_t* mask, int P, uint64_t* bits) {
+  if (!mask || !bits || P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_ARG;
+  uint64_t b = 0;
+  for (int p = 0; p < P; ++p) {
+    if (mask[p] > 1) return DITA_ERR_ARG;
+    b |= uint64_t(mask[p]) << p;
+  }
+  *bits = b;
+  return DITA_OK;
+}
+
+int dita_mask_from_bits(uint64_t bits, int P, uint8_t* mask) {
+  if (!mask || P < 1 || P > DITA_MAX_PARTITIONS) return DITA_ERR_ARG;
+  if (P < 64 && (bits >> P) != 0) return DITA_ERR_ARG;
+  for (int p = 0; p < P; ++p) mask[p] = uint8_t((bits >> p) & 1);
+  return DITA_OK;
+}
+
+int dita_plan_bits(const dita_plan* plan, const dita_state_cache* cache, int64_t step,
+                   uint64_t* reuse_bits) {
+  if (!reuse_bits) return DITA_ERR_ARG;
+  uint8_t m[DITA_MAX_PARTITIONS];
+  const int st = dita_plan_mask(plan, cache, step, m);
+  if (st) return st;
+  return dita_mask_to_bits(m, plan->P, reuse_bits);
+}
+
 int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
                    const void* const* v_list, const int64_t* nk_list, const uint8_t* reuse_mask,
                    int64_t step, void* o, float* lse, void* stream, dita_step_info* info) {

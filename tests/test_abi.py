@@ -81,6 +81,34 @@ def test_planner_matches_oracle_on_random_plans():
         assert np.array_equal(_lib_mask(plan, s), oracle_plan_mask(plan, s)), (plan, s)
 
 
+def test_planner_bitmask_encoding_matches_oracle():
+    """The 64-bit mask encoding: bit p of the word is byte p of the oracle's mask."""
+    rng = np.random.default_rng(5)
+    for trial in range(500):
+        P = int(rng.integers(1, 65))
+        plan = OraclePlan(P=P, q=int(rng.integers(0, P)), policy=int(rng.integers(0, 4)),
+                          radius=int(rng.integers(0, 10)), radius_end=int(rng.integers(0, 10)),
+                          k_nearest=int(rng.integers(0, P + 1)), anchor_period=int(rng.integers(0, 6)),
+                          total_steps=int(rng.integers(1, 60)), seed=int(rng.integers(0, 2**32)))
+        step = int(rng.integers(0, 60))
+        ref = oracle_plan_mask(plan, step)
+        want = sum(int(b) << p for p, b in enumerate(ref))
+        cp = dita.Plan(plan.P, plan.q, plan.policy, plan.radius, plan.radius_end, plan.k_nearest,
+                       plan.anchor_period, plan.total_steps, plan.seed)
+        assert dita.dita_plan_bits(cp, step) == want, trial
+        back = (ctypes.c_uint8 * P)()
+        assert lib.dita_mask_from_bits(want, P, back) == 0 and list(back) == list(ref)
+        bits = ctypes.c_uint64()
+        assert lib.dita_mask_to_bits((ctypes.c_uint8 * P)(*ref), P, ctypes.byref(bits)) == 0
+        assert bits.value == want
+    out = (ctypes.c_uint8 * 4)()
+    assert lib.dita_mask_from_bits(1 << 4, 4, out) == dita.DITA_ERR_ARG      # a bit past P
+    assert lib.dita_mask_to_bits((ctypes.c_uint8 * 4)(0, 2, 0, 0), 4, ctypes.byref(ctypes.c_uint64())) == dita.DITA_ERR_ARG
+    assert lib.dita_mask_from_bits(0, 65, out) == dita.DITA_ERR_ARG
+    full = (ctypes.c_uint8 * 64)()
+    assert lib.dita_mask_from_bits(2**64 - 1, 64, full) == 0 and sum(full) == 64
+
+
 def test_planner_rejects_bad_plans():
     out = (ctypes.c_uint8 * 64)()
     for bad in [dita.Plan(0, 0, 0, 0, 0, 0, 0, 1, 0), dita.Plan(65, 0, 0, 0, 0, 0, 0, 1, 0),
