@@ -247,10 +247,10 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
         e.record(stream)
         return b.elapsed_ms(e) / n
 
+    views = [([c.slot(p)[0] for p in range(wl.P)], [c.slot(p)[1] for p in range(wl.P)]) for c in caches]
+
     def merge(i):
-        c = caches[i]
-        dita.dita_state_merge([c.slot(p)[0] for p in range(wl.P)], [c.slot(p)[1] for p in range(wl.P)],
-                              o=o, lse=lse, stream=stream)
+        dita.dita_state_merge(views[i][0], views[i][1], o=o, lse=lse, stream=stream)
 
     def copy(i):   # slot 0 of cache i -> slot 1 of cache (i+1): one state read and one written
         src = caches[i].slot(0)

@@ -302,6 +302,8 @@ class StateCache:
                    "dita_state_cache_init_pool")
         self.handle = h.value
         self._host = {}
+        # partition p owns slot p unless the cache is pooled: the views never change
+        self._views = None if slots is not None else [self._slot_views(p) for p in range(P)]
 
     def _slot_views(self, p: int):
         torch = _torch()
@@ -319,7 +321,7 @@ class StateCache:
 
     def slot(self, p: int):
         """Views (O_p, LSE_p) of the device memory of partition p's slot."""
-        return self._slot_views(p)
+        return self._views[p] if self._views is not None else self._slot_views(p)
 
     def offload(self, p: int, stream=None):
         """Move leader p's state to pinned host memory (copies on ``stream``)."""
