@@ -157,3 +157,69 @@ def test_attn_partial_peaked_scores_all_waves(dev, D):
                                     to_dev(v, "bf16", dev))
     o_ref, lse_ref = partial_state(q, k, v)
     assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "peaked scores")
+
+
+def test_attn_partial_largest_key_slice(dev):
+    """The largest partition one head may hold: nk * D * 2 bytes just under 2^31
+    (the kernel addresses a head's K and V through 32-bit buffer records).  Keys
+    near the very end carry the largest scores, so a misread tail would show."""
+    import partial_state_reuse_amd as dita
+    D, nq = 128, 40
+    nk = (1 << 31) // (D * 2) - 1
+    say(f"attn_partial largest key slice nk={nk}")
+    rng = np.random.default_rng(12)
+    q = round_bf16(rng.standard_normal((1, 1, nq, D), dtype=np.float32))
+    blk = 1 << 20                                   # a random block of keys, repeated
+    reps = -(-nk // blk)
+    k = np.tile(round_bf16(rng.standard_normal((1, 1, blk, D), dtype=np.float32)), (1, 1, reps, 1))[:, :, :nk]
+    v = np.tile(round_bf16(rng.standard_normal((1, 1, blk, D), dtype=np.float32) * np.float32(0.5)),
+                (1, 1, reps, 1))[:, :, :nk]
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    k[0, 0, nk - nq:] = round_bf16(3.0 * q[0, 0])   # key nk-nq+i aligns with query i
+    o, lse = dita.dita_attn_partial(to_dev(q, "bf16", dev), to_dev(k, "bf16", dev),
+                                    to_dev(v, "bf16", dev))
+    # the oracle over key chunks, composed exactly (merge of partial states)
+    o_ref, lse_ref = merge_states([partial_state(q, k[:, :, a:a + blk], v[:, :, a:a + blk])
+                                   for a in range(0, nk, blk)])
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "largest key slice")
+    lse_host = to_host(lse)[0, 0]
+    assert np.all(lse_host > 20.0)                  # the planted tail keys dominate every row
+
+
+def test_attn_partial_most_heads(dev):
+    """B * H = 65535, the most (batch, head) pairs a launch takes."""
+    import partial_state_reuse_amd as dita
+    say("attn_partial B*H = 65535")
+    rng = np.random.default_rng(13)
+    q, k, v = _inputs(rng, 3, 21845, 33, 17, 64, "bf16", scale=1.5)
+    o, lse = dita.dita_attn_partial(to_dev(q, "bf16", dev), to_dev(k, "bf16", dev),
+                                    to_dev(v, "bf16", dev))
+    o_ref, lse_ref = partial_state(q, k, v)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "B*H = 65535")
+
+
+def test_step_with_most_partitions(dev):
+    """A rank-step over 64 partitions (the most a cache holds), ragged lengths, then
+    a mixed reuse step."""
+    import torch
+    import partial_state_reuse_amd as dita
+    from oracle import StateCache as OracleCache
+    from oracle import attn_step as oracle_step
+    say("attn_step P = 64")
+    rng = np.random.default_rng(14)
+    P, H, nq, D = 64, 2, 70, 64
+    lengths = [int(x) for x in rng.integers(1, 90, P)]
+    q = round_bf16(rng.standard_normal((1, H, nq, D), dtype=np.float32) * np.float32(1.2))
+    ks = [round_bf16(rng.standard_normal((1, H, n, D), dtype=np.float32) * np.float32(1.2)) for n in lengths]
+    vs = [round_bf16(rng.standard_normal((1, H, n, D), dtype=np.float32) * np.float32(0.5)) for n in lengths]
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    ref = OracleCache(P)
+    qd = to_dev(q, "bf16", dev)
+    kd = [to_dev(x, "bf16", dev) for x in ks]
+    vd = [to_dev(x, "bf16", dev) for x in vs]
+    for s, mask in enumerate([np.zeros(P, np.uint8), (rng.random(P) < 0.5).astype(np.uint8)]):
+        o, lse, info = dita.dita_attn_step(cache, qd, kd, vd, mask, s)
+        o_ref, lse_ref, nf = oracle_step(ref, q, ks, vs, mask, s)
+        assert info.n_fresh == nf
+        assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", f"P=64 step {s}")
