@@ -176,7 +176,8 @@ int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, 
  * allocated, and must not be written, until the state is fetched, stored over
  * or invalidated.  Stream-ordered device-to-host copies; in a pooled cache the
  * slot returns to the pool.  The state stays valid: a step that reuses it, or
- * dita_state_cache_fetch, copies it back.  Page section: State-Centric
+ * dita_state_cache_fetch, copies it back; when that happens on another stream
+ * the caller orders it after this call's stream.  Page section: State-Centric
  * Parallel Runtime > Pipeline Orchestration ("reuse" operations load cached
  * states).  DITA_ERR_STATE unless p leads a valid group held on the device.
  */
