@@ -21,8 +21,9 @@
  *  - Every argument is validated before any HIP call or kernel launch; on an
  *    error nothing is launched and no output, slot or metadata changes.  A
  *    HIP runtime failure (DITA_ERR_HIP) part-way through a call that enqueues
- *    several operations may leave the earlier ones enqueued; a step's cache
- *    metadata is then left as it was before the call.
+ *    several operations may leave the earlier ones enqueued (a step that fails
+ *    after its attention launch has already recorded the fresh states in the
+ *    cache metadata); the stream should then be treated as failed.
  *  - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and is asynchronous: no call synchronises the host.  Faults of
  *    the kernels surface at the caller's next synchronisation.
