@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--fresh-weight", type=float, default=0.0,
                     help="error planner: groups holding a partition of at least this "
                          "contribution are always computed (0: off)")
+    ap.add_argument("--fixed-radius", type=int, default=-1,
+                    help="replace the workload's mask schedule by a fixed distance radius")
     ap.add_argument("--planner-anchor", type=int, default=0,
                     help="error planner: anchor period (0: only the cold step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -418,6 +420,10 @@ def main():
     from workloads import Inputs
 
     wl = workloads.get(args.workload)
+    if args.fixed_radius >= 0:
+        # a fixed distance schedule on the same shape and inputs (no anchors after step 0)
+        wl = workloads.get(args.workload, policy=workloads.POLICY_DIST, radius=args.fixed_radius,
+                           anchor_period=0)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     n_sched = wl.steps
