@@ -148,3 +148,43 @@ def test_pooled_cache_chunked_fill_and_steps(dev):
 def ctypes_shape(cache):
     import ctypes
     return ctypes.byref(cache.shape)
+
+
+def test_everything_together_matches_oracle(dev):
+    """Random masks, composition ahead of each step, random moves of group states to
+    the host, a pooled cache and a side stream with pre-merge, over 14 steps with
+    drifting K/V: every output against the fp64 oracle."""
+    import torch
+    import partial_state_reuse_amd as dita
+    from oracle import compose_runs as oracle_compose_runs
+    rng = np.random.default_rng(34)
+    lengths = [150, 96, 210, 64, 180, 120, 240, 77]
+    P, H, nq, D = len(lengths), 2, 190, 128
+    q, ks, vs = _inputs(rng, H, nq, lengths, D)
+    qd = to_dev(q, "bf16", dev)
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=P)
+    ref = OracleCache(P)
+    side = torch.cuda.Stream(device=dev)
+    masks = []
+    for s in range(14):
+        m = (rng.random(P) < 0.65).astype(np.uint8)
+        m[0] = 0
+        if s % 6 == 0:
+            m[:] = 0
+        masks.append(m)
+    for s, m in enumerate(masks):
+        kd, vd = _dev(ks, dev), _dev(vs, dev)
+        o, lse, info = dita.dita_attn_step(cache, qd, kd, vd, m, s, side_stream=side)
+        o_ref, lse_ref, nf = oracle_step(ref, q, ks, vs, m, s)
+        assert info.n_fresh == nf
+        torch.cuda.synchronize()
+        assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", f"step {s}")
+        if s + 1 < len(masks):
+            assert cache.compose_runs(masks[s + 1]) == oracle_compose_runs(ref, masks[s + 1])
+            for p in ref.leaders():
+                if ref.group_range(p)[1] > p and rng.random() < 0.5:
+                    cache.offload(p)
+        on_dev, on_host, free = cache.residency()
+        assert on_dev + on_host == ref.live_states() and on_dev + free == P
+        ks = [round_bf16(0.98 * x + 0.2 * rng.standard_normal(x.shape)) for x in ks]
+        vs = [round_bf16(0.98 * x + 0.1 * rng.standard_normal(x.shape)) for x in vs]
