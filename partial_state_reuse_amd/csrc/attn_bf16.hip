@@ -61,8 +61,9 @@
 //   in LDS) only when some lane's partial sum exceeds 2^16, i.e. when a score
 //   rose well above the running max.  The denominator sums the fp32
 //   probabilities (LSE keeps fp32 accuracy); P V uses them rounded to bf16.
-// * Ragged tails: query rows past Nq load a clamped row and are not stored;
-//   key rows past nk read as zero and their scores are set to -inf.
+// * Ragged tails: query rows past Nq read as zero (a buffer resource whose
+//   records end at Nq) and are not stored; key rows past nk read as zero and
+//   their scores are set to -inf.
 //
 // Measured on one MI355X (4725 x 4725 per head, D = 128, 120 heads): 1.15
 // PFLOP/s, against 1.08 for a four-wave kernel without phase synchronisation
@@ -89,7 +90,6 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the r
 constexpr float kFastLimit = 65536.0f; // largest per-lane partial sum the fast path accepts
 constexpr int kXcds = 8;
 
-__device__ inline u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ inline f32x16 zero16() {
@@ -314,13 +314,22 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
   int qrow[QB];
   bf16x8 qf[QB][NKK];
+  // Q of this query tile through a buffer resource whose records end at row Nq:
+  // rows past it read as zero, so their (discarded) MFMAs multiply zeros.
+  const int64_t tile_row0 = int64_t(qt) * T::BM;
+  const int64_t rows_left = int64_t(Nq) - tile_row0;
+  const __amdgpu_buffer_rsrc_t rq =
+      tile_rsrc(reinterpret_cast<const char*>(qp + tile_row0 * D), 0, 0,
+                uint32_t((rows_left < T::BM ? rows_left : T::BM) * D * 2));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     qrow[qb] = qt * T::BM + (wave * QB + qb) * 32 + m32;
-    const int qrow_c = qrow[qb] < Nq ? qrow[qb] : Nq - 1;
+    const int lrow = (wave * QB + qb) * 32 + m32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qf[qb][kk] = as_bf16x8(load16(qp + int64_t(qrow_c) * D + kk * 16 + 8 * hh));
+      qf[qb][kk] = as_bf16x8(__builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rq, uint32_t(lrow * D * 2 + (kk * 16 + 8 * hh) * 2), 0, 0)));
   }
 #pragma unroll
   for (int st0 = 0; st0 < 3; ++st0)
