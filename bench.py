@@ -371,6 +371,9 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None
                 d = float(chg[2].item())
                 planner.observe(s, d)
                 out["planner"]["local_change"].append(d)
+            if compose_ahead and s + 1 < wl.steps:
+                # the planner's next mask is known once this step's change is observed
+                cache.compose_runs(planner.mask(s + 1, cache=cache)[0], stream=stream)
         elif compose_ahead and s + 1 < wl.steps:
             cache.compose_runs(dita.dita_plan_mask(plan, s + 1, cache), stream=stream)
         dita.dita_attn_step(ref, q, ks, vs, all_fresh, s, o=o_ref, lse=lse_ref, stream=stream)
