@@ -90,6 +90,8 @@ def parse():
                          "contribution are always computed (0: off)")
     ap.add_argument("--fixed-radius", type=int, default=-1,
                     help="replace the workload's mask schedule by a fixed distance radius")
+    ap.add_argument("--planner-compose", type=int, default=0, choices=(0, 1),
+                    help="error planner: compose the runs its next mask reuses after each step")
     ap.add_argument("--planner-anchor", type=int, default=0,
                     help="error planner: anchor period (0: only the cold step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -371,7 +373,7 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None
                 d = float(chg[2].item())
                 planner.observe(s, d)
                 out["planner"]["local_change"].append(d)
-            if compose_ahead and s + 1 < wl.steps:
+            if eplan.get("compose_ahead") and s + 1 < wl.steps:
                 # the planner's next mask is known once this step's change is observed
                 cache.compose_runs(planner.mask(s + 1, cache=cache)[0], stream=stream)
         elif compose_ahead and s + 1 < wl.steps:
@@ -573,7 +575,8 @@ def main():
         eplan = None
         if args.planner == "error":
             eplan = {"group_size": args.group_size, "budget": args.budget,
-                     "anchor_period": args.planner_anchor, "fresh_weight": args.fresh_weight}
+                     "anchor_period": args.planner_anchor, "fresh_weight": args.fresh_weight,
+                     "compose_ahead": bool(args.planner_compose)}
         result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream,
                                           compose_ahead=bool(args.compose_ahead), eplan=eplan)
     if not args.no_cpu_baseline:
