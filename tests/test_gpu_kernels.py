@@ -223,3 +223,23 @@ def test_step_with_most_partitions(dev):
         o_ref, lse_ref, nf = oracle_step(ref, q, ks, vs, mask, s)
         assert info.n_fresh == nf
         assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", f"P=64 step {s}")
+
+
+def test_step_with_one_partition(dev):
+    """P = 1: the step's merge is the identity on the one state (O bit for bit, LSE
+    to fp32 rounding of exp2/log2 of a zero offset), and an all-reuse step
+    returns the same output again."""
+    import torch
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(15)
+    q, k, v = _inputs(rng, 1, 3, 150, 333, 128, "bf16", scale=1.5)
+    qd, kd, vd = to_dev(q, "bf16", dev), to_dev(k, "bf16", dev), to_dev(v, "bf16", dev)
+    cache = dita.StateCache(1, 3, 150, 128, torch.bfloat16, 1, device=dev)
+    o, lse, info = dita.dita_attn_step(cache, qd, [kd], [vd], np.zeros(1, np.uint8), 0)
+    assert info.n_fresh == 1 and info.merge_sources == 1
+    so, sl = cache.slot(0)
+    assert bool((o == so).all()) and max_abs(to_host(lse), to_host(sl)) <= 1e-6
+    o_ref, lse_ref = partial_state(q, k, v)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "P = 1")
+    o2, l2, info = dita.dita_attn_step(cache, qd, [None], [None], np.ones(1, np.uint8), 1)
+    assert info.n_fresh == 0 and bool((o2 == o).all()) and bool((l2 == lse).all())
