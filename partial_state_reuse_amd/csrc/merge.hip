@@ -114,11 +114,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
     if (c == 0) lse[row] = -INFINITY;
     return;
   }
-  // w_p = exp(LSE_p - M) = exp2((LSE_p - M) log2 e); 0 for LSE_p = -inf.
-  const float mb = -M * kLog2e;
+  // w_p = exp(LSE_p - M) = exp2((LSE_p - M) log2 e); 0 for LSE_p = -inf.  The
+  // difference is taken first, so the largest state weighs exactly 1 (a
+  // one-state merge returns its input unchanged).
   float L = 0.0f;
   auto accumulate = [&](u32x4 r, float l) {
-    const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(l, kLog2e, mb));
+    const float w = __builtin_amdgcn_exp2f((l - M) * kLog2e);
     L += w;
     float x[VN];
     Vec<T>::unpack(r, x);

@@ -116,7 +116,7 @@ def test_state_merge_single_state_is_identity_bitwise(dev):
     os_, ls = _states(rng, 1, 1, 2, 50, 128, "bf16")
     o, lse = dita.dita_state_merge([to_dev(os_[0], "bf16", dev)], [to_dev(ls[0], "f32", dev)])
     assert np.array_equal(to_host(o), os_[0].astype(np.float64))
-    assert max_abs(to_host(lse), ls[0]) <= 1e-6
+    assert np.array_equal(to_host(lse), ls[0].astype(np.float32).astype(np.float64))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -226,9 +226,8 @@ def test_step_with_most_partitions(dev):
 
 
 def test_step_with_one_partition(dev):
-    """P = 1: the step's merge is the identity on the one state (O bit for bit, LSE
-    to fp32 rounding of exp2/log2 of a zero offset), and an all-reuse step
-    returns the same output again."""
+    """P = 1: the step's merge is the identity on the one state (bit for bit), and
+    an all-reuse step returns the same output again."""
     import torch
     import partial_state_reuse_amd as dita
     rng = np.random.default_rng(15)
@@ -238,7 +237,7 @@ def test_step_with_one_partition(dev):
     o, lse, info = dita.dita_attn_step(cache, qd, [kd], [vd], np.zeros(1, np.uint8), 0)
     assert info.n_fresh == 1 and info.merge_sources == 1
     so, sl = cache.slot(0)
-    assert bool((o == so).all()) and max_abs(to_host(lse), to_host(sl)) <= 1e-6
+    assert bool((o == so).all()) and bool((lse == sl).all())
     o_ref, lse_ref = partial_state(q, k, v)
     assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "P = 1")
     o2, l2, info = dita.dita_attn_step(cache, qd, [None], [None], np.ones(1, np.uint8), 1)
