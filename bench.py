@@ -416,6 +416,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): sharding the "
               "rank-step across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
