@@ -61,13 +61,14 @@ def test_offload_fetch_roundtrip_bitwise(dev):
     assert cache.residency() == (4, 0, 0)
 
 
-@pytest.mark.parametrize("mode", ["stream", "side", "side_premerge"])
-def test_step_fetches_offloaded_states(dev, mode):
+@pytest.mark.parametrize("mode,D", [("stream", 128), ("side", 128), ("side_premerge", 128),
+                                    ("side", 64)])
+def test_step_fetches_offloaded_states(dev, mode, D):
     import torch
     import partial_state_reuse_amd as dita
     rng = np.random.default_rng(31)
     lengths = [200, 129, 256, 70, 333, 190]
-    P, H, nq, D = len(lengths), 3, 230, 128
+    P, H, nq = len(lengths), 3, 230
     q, ks, vs = _inputs(rng, H, nq, lengths, D)
     qd, kd, vd = to_dev(q, "bf16", dev), _dev(ks, dev), _dev(vs, dev)
     _, ks1, vs1 = _inputs(np.random.default_rng(32), H, nq, lengths, D)
@@ -188,3 +189,38 @@ def test_everything_together_matches_oracle(dev):
         assert on_dev + on_host == ref.live_states() and on_dev + free == P
         ks = [round_bf16(0.98 * x + 0.2 * rng.standard_normal(x.shape)) for x in ks]
         vs = [round_bf16(0.98 * x + 0.1 * rng.standard_normal(x.shape)) for x in vs]
+
+
+def test_sixty_four_partitions_with_groups_and_offload(dev):
+    """The largest cache (64 partitions, pooled): a growing near set recomputed, with
+    composition ahead of each step and the far groups moved to the host, against
+    the oracle."""
+    import torch
+    import partial_state_reuse_amd as dita
+    from oracle import compose_runs as oracle_compose_runs
+    rng = np.random.default_rng(35)
+    P, H, nq, D = 64, 2, 96, 64
+    lengths = [int(x) for x in rng.integers(16, 80, P)]
+    q, ks, vs = _inputs(rng, H, nq, lengths, D)
+    qd, kd, vd = to_dev(q, "bf16", dev), _dev(ks, dev), _dev(vs, dev)
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=P)
+    ref = OracleCache(P)
+    masks = [np.zeros(P, np.uint8)]
+    for s in range(1, 6):
+        m = np.ones(P, np.uint8)
+        m[: 2 + s] = 0                                  # a growing near set recomputed
+        masks.append(m)
+    side = torch.cuda.Stream(device=dev)
+    for s, m in enumerate(masks):
+        o, lse, info = dita.dita_attn_step(cache, qd, kd, vd, m, s, side_stream=side)
+        o_ref, lse_ref, nf = oracle_step(ref, q, ks, vs, m, s)
+        assert info.n_fresh == nf
+        torch.cuda.synchronize()
+        assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", f"P=64 step {s}")
+        if s + 1 < len(masks):
+            cache.compose_runs(masks[s + 1])
+            oracle_compose_runs(ref, masks[s + 1])
+            for p in ref.leaders():
+                if ref.group_range(p)[1] > p:
+                    cache.offload(p)
+            assert cache.residency()[1] == sum(1 for p in ref.leaders() if ref.group_range(p)[1] > p)
