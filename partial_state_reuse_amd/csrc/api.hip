@@ -3,6 +3,17 @@
 // Every entry point validates all of its arguments before it makes any HIP
 // call, so a rejected call launches nothing and changes nothing.  Launches are
 // asynchronous on the caller's stream; the library never synchronises.
+//
+// The cache handle keeps host metadata only: per partition its validity, the
+// step that wrote its state, its group (composed partitions share the state
+// in the group's first slot; the DiTango page, State-Centric Parallel Runtime >
+// Dynamic Group Compose), the physical slot holding its state (fixed, or taken
+// from a pool) and, for a state moved to the host, the caller's buffers.  A
+// step widens the caller's mask to whole groups, takes physical slots for what
+// it computes or brings back, launches one grouped attention kernel writing
+// straight into the slots, and merges one state per group; with a side stream
+// it copies host-resident states back, and may pre-merge the reused ones,
+// beside the attention (Pipeline Orchestration on the same page).
 
 #include <hip/hip_runtime.h>
 
