@@ -176,15 +176,22 @@ def _blas_info():
 
 
 def cpu_baseline(inp, wl, budget_s: float):
-    """The fp64 oracle's rank-step, timed as it stands on the host cores, on a head
-    sample of a non-anchor step (fresh blocks + P-way merge)."""
+    """The fp64 oracle's rank-step, timed as it stands on the host cores: a
+    non-anchor step (fresh blocks + P-way merge), its heads spread over a pool of
+    worker threads with one BLAS thread each (numpy releases the interpreter lock
+    in its matrix products and element-wise kernels; the oracle's exp is
+    single-threaded per call, so the parallel width comes from the heads).  Heads
+    run in waves of `workers` until about budget_s has passed; one head is also
+    timed alone on one core."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import Plan, StateCache, attn_step, plan_mask
     from workloads import split_parts
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    cpus = len(os.sched_getaffinity(0))
+    workers = max(1, min(cpus, 16, wl.H))
     plan = Plan(**wl.plan_fields())
     # The first step index whose mask is not all-fresh with every slot filled.
     s = next(i for i in range(1, wl.steps + 1)
@@ -192,35 +199,58 @@ def cpu_baseline(inp, wl, budget_s: float):
     mask = plan_mask(plan, s % wl.steps, np.ones(wl.P, np.uint8))
     k, v = inp.kv(s % wl.steps)
     kp, vp = split_parts(k, wl), split_parts(v, wl)
-    rng = np.random.default_rng(0)
-    heads_done, elapsed, flops = 0, 0.0, 0.0
-    for h in range(wl.H):
+    block_flops = 4.0 * wl.B * wl.Nq * wl.D * sum(wl.Nk for p in range(wl.P) if mask[p] == 0)
+
+    def setup(h):
+        rng = np.random.default_rng(h)
         cache = StateCache(wl.P)
         for p in range(wl.P):   # reused slots: any state of the right shape (untimed)
             cache.store(p, (rng.standard_normal((wl.B, 1, wl.Nq, wl.D)),
                             rng.standard_normal((wl.B, 1, wl.Nq)) + 9.0), 0)
-        qh = inp.q[:, h:h + 1]
-        kh = [x[:, h:h + 1] for x in kp]
-        vh = [x[:, h:h + 1] for x in vp]
+        return cache
+
+    def one(h, cache):
+        return attn_step(cache, inp.q[:, h:h + 1], [x[:, h:h + 1] for x in kp],
+                         [x[:, h:h + 1] for x in vp], mask, s)
+
+    class _Null:
+        def __enter__(self):
+            return self
+
+        def __exit__(self, *a):
+            return False
+
+    limit = threadpool_limits(1) if threadpool_limits else _Null()
+    with limit:
+        c0 = setup(0)
         t0 = time.perf_counter()
-        _, _, nf = attn_step(cache, qh, kh, vh, mask, s)
-        elapsed += time.perf_counter() - t0
-        flops += 4.0 * wl.B * wl.Nq * wl.D * sum(wl.Nk for p in range(wl.P) if mask[p] == 0)
-        heads_done += 1
-        if elapsed >= budget_s:
-            break
-    host = {"affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
-            "blas": _blas_info()}
+        one(0, c0)
+        single_s = time.perf_counter() - t0
+        heads_done, elapsed = 0, 0.0
+        with ThreadPoolExecutor(workers) as ex:
+            while heads_done < wl.H and elapsed < budget_s:
+                wave = list(range(heads_done, min(wl.H, heads_done + workers)))
+                caches = [setup(h) for h in wave]
+                t0 = time.perf_counter()
+                list(ex.map(lambda a: one(*a), zip(wave, caches)))
+                elapsed += time.perf_counter() - t0
+                heads_done += len(wave)
+    host = {"affinity_cpus": cpus, "cpu_model": _cpu_model(), "blas": _blas_info()}
     return {
-        "value": flops / elapsed / 1e12,
+        "value": block_flops * heads_done / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas_threads),
+        "cores": int(workers),
         "kind": "oracle",
         "host": host,
+        "workers": workers,
+        "blas_threads_per_worker": 1,
         "ms_per_step": elapsed / heads_done * wl.H * 1e3,
+        "single_core": {"heads": 1, "s": single_s, "TFLOPs": block_flops / single_s / 1e12,
+                        "ms_per_step": single_s * wl.H * 1e3},
         "sample": (f"fp64 numpy oracle rank-step (schedule step {s % wl.steps}: "
                    f"{int((mask == 0).sum())} fresh blocks + {wl.P}-way merge) on {heads_done} of "
-                   f"{wl.H} heads, {elapsed:.1f} s; ms_per_step extrapolated to all heads"),
+                   f"{wl.H} heads in waves of {workers} worker threads with one BLAS thread each, "
+                   f"{elapsed:.1f} s; ms_per_step scaled to all heads"),
     }
 
 
@@ -271,6 +301,59 @@ def isolated_bandwidth(dita, wl, tdt, dev, stream, q, n_caches: int = 4, reps: i
                        "frac_hbm_peak": c_gbs / PEAK_HBM_GBS},
         "note": f"rotating over {n_caches} caches of {wl.P} slots ({n_caches * caches[0].buffer.numel() / 1e9:.2f} GB)",
     }
+
+
+def hbm_ceiling(dev, gib: int = 2, reps: int = 5):
+    """An attainable HBM bandwidth on this GPU: torch's device-to-device copy of a
+    `gib` GiB buffer (read + write), best of `reps`, beside the vendor's 8 TB/s."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        dst.copy_(src)
+        e.record()
+        e.synchronize()
+        ms = b.elapsed_time(e)
+        best = ms if best is None else min(best, ms)
+    gbs = 2 * n / (best / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"[bench] HBM ceiling: torch copy of {gib} GiB at {gbs:.0f} GB/s")
+    return {"GBps": gbs, "frac_vendor_peak": gbs / PEAK_HBM_GBS,
+            "how": f"torch device copy of {gib} GiB (read + write), best of {reps}"}
+
+
+def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 10):
+    """One dita_attn_partial call on one 75,600-token block (the rank's queries against
+    one partition, all heads), as a caller would make it alone: HIP events on the
+    launch stream around each call, median over `reps` calls."""
+    import torch
+    ks, vs = kv0
+    o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
+    lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        dita.dita_attn_partial(q, ks[1], vs[1], o=o, lse=lse, stream=stream)
+    times = []
+    for i in range(reps):
+        b, e = dita.Event(), dita.Event()
+        b.record(stream)
+        dita.dita_attn_partial(q, ks[1 + i % (wl.P - 1)], vs[1 + i % (wl.P - 1)], o=o, lse=lse,
+                               stream=stream)
+        e.record(stream)
+        times.append(b.elapsed_ms(e))
+    ms = float(np.median(times))
+    tf = wl.block_flops() / (ms / 1e3) / 1e12
+    log(f"[bench] lone dita_attn_partial: {ms:.3f} ms = {tf:.0f} TFLOP/s")
+    return {"ms_median": ms, "ms_min": float(np.min(times)), "flops": wl.block_flops(),
+            "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS,
+            "note": "one block, all heads: Q [1,40,4725,128] against one 4725-key partition"}
 
 
 def offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan, reps: int = 3):
@@ -560,15 +643,22 @@ def main():
             "avg_launch_ms": attn_s * 1e3 / max(launches, 1),
             "flops_per_launch": fresh_flops / max(launches, 1),
         },
-        "merge": {
-            "kernel": "merge_kernel", "bound": "hbm",
-            "achieved": merge_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": merge_gbs / PEAK_HBM_GBS, "bytes_per_launch": merge_bytes / K,
+        "merge_in_step": {
+            "kernel": "merge_kernel", "bound": None,
+            "achieved": merge_gbs, "unit": "GB/s", "bytes_per_launch": merge_bytes / K,
             "traffic": traffic_merge,
             "avg_launch_ms": sum(merge_ms) / K,
+            "note": ("algorithmic bytes / time of the step's final merge; it reads states the "
+                     "attention launch has just written, which the 256 MB last-level cache "
+                     "partly serves, so this is not an HBM figure (isolated.merge is)"),
         },
     }
     result["isolated"] = isolated_bandwidth(dita, wl, tdt, dev, stream, q)
+    result["hbm_ceiling"] = hbm_ceiling(dev)
+    iso_m = result["isolated"]["merge"]
+    iso_m["frac_measured_ceiling"] = iso_m["GBps"] / result["hbm_ceiling"]["GBps"]
+    if wl.dtype == "bf16":
+        result["lone_attn_partial"] = lone_partial(dita, wl, tdt, dev, stream, q, kv[0])
     if wl.steps > 1 and n_res > 1:
         result["offload"] = offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan)
     if args.trajectory:

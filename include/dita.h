@@ -28,7 +28,9 @@
  *    stream) and is asynchronous: no call synchronises the host.  Faults of
  *    the kernels surface at the caller's next synchronisation.
  *  - The caller owns every device buffer, the state-cache buffer included.
- *    The library owns only the host-side cache handle.
+ *    The library owns only the host-side cache handle (and its HIP events),
+ *    and the transient scratch of dita_state_change, taken from HIP's
+ *    stream-ordered allocator and returned within the call.
  *  - Layouts are contiguous row-major: Q and O are [B, H, Nq, D]; K_p and
  *    V_p are [B, H, Nk_p, D]; LSE arrays are float32 [B, H, Nq].  O and O_p
  *    have the input dtype; LSE is always float32 and uses the natural log.
@@ -169,6 +171,20 @@ int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P
  * launch, when none is free).  Page section: State-Centric Parallel Runtime >
  * Dynamic Group Compose (composition relieves memory pressure) -- with a pool,
  * the states a cache no longer holds are device memory the next state can use.
+ *
+ * Stream order of a pooled cache: because the library moves physical slots
+ * between partitions, it orders the device work on each slot itself.  Every
+ * call that enqueues work on pooled slots (store, load, offload, fetch,
+ * compose, compose_runs, the steps, dita_state_cache_contrib) makes its
+ * stream wait for the last work enqueued on each slot it touches when that
+ * work was enqueued on another stream (hipStreamWaitEvent on an event the
+ * handle records; events are created on first use and destroyed by
+ * dita_state_cache_free).  So calls on one pooled handle may use different
+ * streams: the work on any one slot runs in call order.  Work the caller
+ * enqueues itself on slot memory (through dita_state_cache_slot) is outside
+ * this order.  In a cache made by dita_state_cache_init, partition p owns
+ * slot p; ordering calls on different streams is then the caller's concern,
+ * as for any device buffer.
  */
 int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, int P, int S,
                                void* dev_buf, size_t bytes);
@@ -326,7 +342,11 @@ int dita_mask_from_bits(uint64_t bits, int P, uint8_t* mask);
  *                        entries of reused partitions are not read (may be NULL)
  * nk_list          [in]  host array of P key counts (>= 1 where computed)
  * reuse_mask       [in]  host array of P bytes (0 fresh, 1 reuse; other values rejected)
- * o, lse           [out] device final output and LSE
+ * o, lse           [out] device final output and LSE; they may not overlap the
+ *                        cache buffer or each other.  (They may share memory
+ *                        with q or the fresh K/V here, since the merge that
+ *                        writes them follows the attention on `stream`, but
+ *                        not in dita_attn_step_ex with a side stream.)
  * info             [in/out, nullable] step report; its `events` members, when
  *                  non-NULL, are hipEvent_t handles recorded on `stream` at the
  *                  step start, after the fresh-attention launch and at the end.
@@ -368,7 +388,10 @@ int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_
  * the pre-merge before its final merge, so on return every effect is ordered
  * on `stream` as in dita_attn_step.  The result equals dita_attn_step's up to
  * the order of the fp32 sums.  opts == NULL, or no pre-merge taken, is exactly
- * dita_attn_step.
+ * dita_attn_step.  With a side stream given (non-NULL and not `stream`), o and
+ * lse may not overlap q or the K/V of any partition computed fresh, since the
+ * side stream may write them while the attention reads those: DITA_ERR_ARG,
+ * before anything is enqueued.
  */
 typedef struct {
   void* side_stream;     /* hipStream_t for the pre-merge, or NULL                  */
@@ -397,12 +420,15 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
  *   `lse` the LSE the step merged them into.
  * dita_state_change: out[0] = sum (o_new - o_prev)^2, out[1] = sum o_prev^2,
  *   out[2] = sqrt(out[0] / out[1]) (0 when both sums are 0, +inf when only
- *   out[1] is) over all B*H*Nq*D elements, fp64 (the order of the final
- *   per-workgroup additions is not fixed).  roll != 0 also copies (o_new,
- *   lse_new) over (o_prev, lse_prev) in the same pass.  out: device, 3
- *   doubles.  o_new/o_prev: device [B, H, Nq, D] dtype; lse_new/lse_prev:
- *   device [B, H, Nq] float32 (read/written only when rolling; may be NULL
- *   otherwise).  The new and previous buffers must not overlap.
+ *   out[1] is) over all B*H*Nq*D elements, fp64, summed in an order fixed by
+ *   the state's size alone: the result is the same bit for bit on every run.
+ *   roll != 0 also copies (o_new, lse_new) over (o_prev, lse_prev) in the same
+ *   pass.  out: device, 3 doubles.  o_new/o_prev: device [B, H, Nq, D] dtype;
+ *   lse_new/lse_prev: device [B, H, Nq] float32 (read/written only when
+ *   rolling; may be NULL otherwise).  The new and previous buffers must not
+ *   overlap.  The per-workgroup partial sums (at most 16 KB) live in scratch
+ *   taken from HIP's stream-ordered allocator (hipMallocAsync on `stream`)
+ *   and returned to it (hipFreeAsync) within the call.
  */
 int dita_state_contrib(const dita_shape* shape, int P, const float* const* lse_list,
                        const float* lse, double* w_out, void* stream);
@@ -410,6 +436,7 @@ int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, do
                              void* stream);
 int dita_state_change(const dita_shape* shape, const void* o_new, const float* lse_new,
                       void* o_prev, float* lse_prev, int roll, double* out, void* stream);
+
 
 /*
  * Error-guided planner (host only, float64).  Page section: 1. Anchor-Guided

@@ -194,6 +194,30 @@ def _stream(t, stream=None) -> int:
     return stream.cuda_stream
 
 
+def _expect(t, shape, dtype, name: str):
+    """Raise ValueError unless ``t`` has exactly ``shape`` and ``dtype`` (checked before
+    any pointer is taken: the C ABI cannot see buffer sizes)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _same_device(name: str, ref, *ts):
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name}: tensors on {t.device} and {ref.device}")
+
+
+def _check_kv(k, v, B: int, H: int, D: int, dtype, name: str):
+    if k.dim() != 4 or tuple(k.shape[:2]) != (B, H) or k.shape[3] != D or k.shape[2] < 1:
+        raise ValueError(f"{name}: K has shape {tuple(k.shape)}, expected [{B}, {H}, Nk >= 1, {D}]")
+    _expect(k, k.shape, dtype, f"{name} K")
+    _expect(v, k.shape, dtype, f"{name} V")
+
+
 def make_shape(q, scale: float = 0.0) -> Shape:
     """Shape record of a [B, H, Nq, D] query tensor."""
     B, H, Nq, D = q.shape
@@ -213,15 +237,17 @@ def _ptr_array(ptrs: Sequence[Optional[int]]):
 def dita_attn_partial(q, k, v, o=None, lse=None, scale: float = 0.0, stream=None):
     """Fresh state (O_p, LSE_p) of ``q`` [B,H,Nq,D] against one partition ``k``, ``v`` [B,H,Nk,D]."""
     torch = _torch()
-    if k.shape[:2] != q.shape[:2] or v.shape != k.shape or k.shape[3] != q.shape[3]:
-        raise ValueError("q, k, v shapes disagree")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, Nq, D], got shape {tuple(q.shape)}")
     B, H, Nq, D = q.shape
+    _check_kv(k, v, B, H, D, q.dtype, "dita_attn_partial")
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _expect(o, q.shape, q.dtype, "o")
+    _expect(lse, (B, H, Nq), torch.float32, "lse")
+    _same_device("dita_attn_partial", q, k, v, o, lse)
     shape = make_shape(q, scale)
     _check(_lib.dita_attn_partial(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
                                   _ptr(o), _ptr(lse), _stream(q, stream)), "dita_attn_partial")
@@ -235,17 +261,22 @@ def dita_state_merge(o_list: Sequence, lse_list: Sequence, o=None, lse=None, sca
     if len(o_list) != len(lse_list) or not o_list:
         raise ValueError("need equally long, non-empty state lists")
     ref = o_list[0]
-    if o is None:
-        o = torch.empty_like(ref)
-    if lse is None:
-        lse = torch.empty(ref.shape[:3], dtype=torch.float32, device=ref.device)
-    shape = make_shape(ref, scale)
+    if ref.dim() != 4:
+        raise ValueError(f"state outputs must be [B, H, Nq, D], got shape {tuple(ref.shape)}")
     for x in o_list:
         if x.shape != ref.shape or x.dtype != ref.dtype:
             raise ValueError("state outputs must share shape and dtype")
     for x in lse_list:
         if x.shape != ref.shape[:3] or x.dtype != torch.float32:
             raise ValueError("LSE arrays must be float32 [B, H, Nq]")
+    if o is None:
+        o = torch.empty_like(ref)
+    if lse is None:
+        lse = torch.empty(ref.shape[:3], dtype=torch.float32, device=ref.device)
+    _expect(o, ref.shape, ref.dtype, "o")
+    _expect(lse, ref.shape[:3], torch.float32, "lse")
+    _same_device("dita_state_merge", ref, *o_list, *lse_list, o, lse)
+    shape = make_shape(ref, scale)
     P = len(o_list)
     _check(_lib.dita_state_merge(ctypes.byref(shape), P, _ptr_array([_ptr(x) for x in o_list]),
                                  _ptr_array([_ptr(x) for x in lse_list]), _ptr(o), _ptr(lse),
@@ -319,6 +350,17 @@ class StateCache:
         return (o.view(self.dtype).view(s.B, s.H, s.Nq, s.D),
                 lse.view(torch.float32).view(s.B, s.H, s.Nq))
 
+    def state_shape(self):
+        s = self.shape
+        return (s.B, s.H, s.Nq, s.D), (s.B, s.H, s.Nq)
+
+    def _check_state(self, o, lse, what: str):
+        torch = _torch()
+        so, sl = self.state_shape()
+        _expect(o, so, self.dtype, f"{what} O")
+        _expect(lse, sl, torch.float32, f"{what} LSE")
+        _same_device(what, self.buffer, o, lse)
+
     def slot(self, p: int):
         """Views (O_p, LSE_p) of the device memory of partition p's slot."""
         return self._views[p] if self._views is not None else self._slot_views(p)
@@ -346,6 +388,7 @@ class StateCache:
         return a.value, b.value, c.value
 
     def store(self, p: int, o, lse, step: int, stream=None):
+        self._check_state(o, lse, "StateCache.store")
         _check(_lib.dita_state_cache_store(self.handle, p, _ptr(o), _ptr(lse), step,
                                            _stream(o, stream)), "dita_state_cache_store")
 
@@ -356,6 +399,7 @@ class StateCache:
             o = torch.empty((s.B, s.H, s.Nq, s.D), dtype=self.dtype, device=self.buffer.device)
         if lse is None:
             lse = torch.empty((s.B, s.H, s.Nq), dtype=torch.float32, device=self.buffer.device)
+        self._check_state(o, lse, "StateCache.load")
         _check(_lib.dita_state_cache_load(self.handle, p, _ptr(o), _ptr(lse), _stream(o, stream)),
                "dita_state_cache_load")
         return o, lse
@@ -394,6 +438,9 @@ class StateCache:
         torch = _torch()
         if w is None:
             w = torch.empty(self.P, dtype=torch.float64, device=self.buffer.device)
+        _expect(lse, self.state_shape()[1], torch.float32, "StateCache.contrib LSE")
+        _expect(w, (self.P,), torch.float64, "StateCache.contrib w")
+        _same_device("StateCache.contrib", self.buffer, lse, w)
         _check(_lib.dita_state_cache_contrib(self.handle, _ptr(lse), _ptr(w), _stream(lse, stream)),
                "dita_state_cache_contrib")
         return w
@@ -454,10 +501,21 @@ def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reu
     if mask.shape != (P,):
         raise ValueError("reuse mask must have P entries")
     s = cache.shape
+    so, sl = cache.state_shape()
+    _expect(q, so, cache.dtype, "q")
+    for p, (k, v) in enumerate(zip(k_list, v_list)):
+        if (k is None) != (v is None):
+            raise ValueError(f"partition {p}: give both K and V, or neither")
+        if k is not None:
+            _check_kv(k, v, s.B, s.H, s.D, cache.dtype, f"partition {p}")
+            _same_device("dita_attn_step", q, k, v)
     if o is None:
-        o = torch.empty((s.B, s.H, s.Nq, s.D), dtype=cache.dtype, device=q.device)
+        o = torch.empty(so, dtype=cache.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty((s.B, s.H, s.Nq), dtype=torch.float32, device=q.device)
+        lse = torch.empty(sl, dtype=torch.float32, device=q.device)
+    _expect(o, so, cache.dtype, "o")
+    _expect(lse, sl, torch.float32, "lse")
+    _same_device("dita_attn_step", cache.buffer, q, o, lse)
     nk = (ctypes.c_int64 * P)(*[(k.shape[2] if k is not None else 0) for k in k_list])
     info = StepInfo()
     if events is not None:
@@ -479,9 +537,16 @@ def dita_state_contrib(lse_list: Sequence, lse, w=None, stream=None):
     """Device float64 [P]: mean over rows of exp(LSE_p - LSE) for each state's LSE."""
     torch = _torch()
     P = len(lse_list)
+    if lse.dim() != 3:
+        raise ValueError(f"lse must be [B, H, Nq], got shape {tuple(lse.shape)}")
     B, H, Nq = lse.shape
+    _expect(lse, lse.shape, torch.float32, "lse")
+    for i, x in enumerate(lse_list):
+        _expect(x, lse.shape, torch.float32, f"lse_list[{i}]")
     if w is None:
         w = torch.empty(P, dtype=torch.float64, device=lse.device)
+    _expect(w, (P,), torch.float64, "w")
+    _same_device("dita_state_contrib", lse, *lse_list, w)
     shape = Shape(B, H, 64, DITA_F32, Nq, 0.0)   # only B, H, Nq matter here
     _check(_lib.dita_state_contrib(ctypes.byref(shape), P, _ptr_array([_ptr(x) for x in lse_list]),
                                    _ptr(lse), _ptr(w), _stream(lse, stream)), "dita_state_contrib")
@@ -493,10 +558,18 @@ def dita_state_change(o_new, o_prev, lse_new=None, lse_prev=None, roll: bool = F
     """Device float64 [3]: sum (new - prev)^2, sum prev^2 and the relative change
     sqrt of their ratio; with ``roll`` the new state is also copied over prev."""
     torch = _torch()
-    if o_new.shape != o_prev.shape or o_new.dtype != o_prev.dtype:
-        raise ValueError("states must share shape and dtype")
+    if o_new.dim() != 4:
+        raise ValueError(f"states must be [B, H, Nq, D], got shape {tuple(o_new.shape)}")
+    _expect(o_prev, o_new.shape, o_new.dtype, "o_prev")
+    if roll and (lse_new is None or lse_prev is None):
+        raise ValueError("rolling needs lse_new and lse_prev")
+    for t, name in ((lse_new, "lse_new"), (lse_prev, "lse_prev")):
+        if t is not None:
+            _expect(t, o_new.shape[:3], torch.float32, name)
     if out is None:
         out = torch.empty(3, dtype=torch.float64, device=o_new.device)
+    _expect(out, (3,), torch.float64, "out")
+    _same_device("dita_state_change", o_new, o_prev, lse_new, lse_prev, out)
     shape = make_shape(o_new)
     _check(_lib.dita_state_change(ctypes.byref(shape), _ptr(o_new), _ptr(lse_new), _ptr(o_prev),
                                   _ptr(lse_prev), int(bool(roll)), _ptr(out), _stream(o_new, stream)),

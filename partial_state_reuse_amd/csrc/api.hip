@@ -45,6 +45,14 @@ struct dita_state_cache {
   uint8_t on_host[DITA_MAX_PARTITIONS];  // p's state lives in caller host memory
   void* host_o[DITA_MAX_PARTITIONS];
   float* host_lse[DITA_MAX_PARTITIONS];
+  // Pooled caches only: the event recorded after the last device work that
+  // touched each physical slot, and the stream it was recorded on.  Events are
+  // shared by the slots one call touched (reference counted) and created on
+  // first use.
+  int16_t slot_ev[DITA_MAX_PARTITIONS];   // index into ev, -1 if no work is tracked
+  hipEvent_t ev[DITA_MAX_PARTITIONS + 1];
+  void* ev_stream[DITA_MAX_PARTITIONS + 1];
+  int16_t ev_refs[DITA_MAX_PARTITIONS + 1];
 };
 
 namespace {
@@ -190,6 +198,51 @@ int effective_mask(const dita_state_cache* c, const uint8_t* reuse, uint8_t* out
   return DITA_OK;
 }
 
+// Stream order of pooled slots.  A pooled cache hands a physical slot from one
+// partition to another, so work the caller enqueued on one stream for the old
+// owner (a copy to the host, a merge reading it) may still be pending when a
+// call on another stream writes the new owner's state there.  Every call that
+// enqueues device work on pooled slots therefore first makes its stream wait
+// for the last recorded work on each slot it touches (when that was recorded
+// on a different stream), and afterwards records one event on its stream for
+// all of them: device work on one pooled slot runs in call order, whatever the
+// streams.  Unpooled caches skip this (partition p owns slot p; ordering work
+// on a partition's slot is the caller's, as for any device buffer).
+int slots_wait(dita_state_cache* c, hipStream_t s, uint64_t slots) {
+  if (!c->pool) return DITA_OK;
+  uint64_t waited = 0;
+  for (int k = 0; k < c->S; ++k) {
+    if (!((slots >> k) & 1)) continue;
+    const int e = c->slot_ev[k];
+    if (e < 0 || ((waited >> e) & 1) || c->ev_stream[e] == static_cast<void*>(s)) continue;
+    const int st = hip_status(hipStreamWaitEvent(s, c->ev[e], 0));
+    if (st) return st;
+    waited |= uint64_t(1) << e;
+  }
+  return DITA_OK;
+}
+
+int slots_mark(dita_state_cache* c, hipStream_t s, uint64_t slots) {
+  if (!c->pool || !slots) return DITA_OK;
+  // A free event: at most S are referenced by slots, and there are S + 1.
+  int e = 0;
+  while (c->ev_refs[e] > 0) ++e;
+  int st;
+  if (!c->ev[e] && (st = hip_status(hipEventCreateWithFlags(&c->ev[e], hipEventDisableTiming))))
+    return st;
+  if ((st = hip_status(hipEventRecord(c->ev[e], s)))) return st;
+  c->ev_stream[e] = static_cast<void*>(s);
+  for (int k = 0; k < c->S; ++k) {
+    if (!((slots >> k) & 1)) continue;
+    if (c->slot_ev[k] >= 0) --c->ev_refs[c->slot_ev[k]];
+    c->slot_ev[k] = int16_t(e);
+    ++c->ev_refs[e];
+  }
+  return DITA_OK;
+}
+
+uint64_t slot_bit(int k) { return k >= 0 ? uint64_t(1) << k : 0; }
+
 // Compose partitions first..last (validated by the caller: all valid, no
 // group straddling the range) into one group state in slot `first`.
 int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, int* launched) {
@@ -197,10 +250,12 @@ int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, 
   dita::MergeSrc src;
   int n = 0;
   int64_t oldest = c->stamp[first];
+  uint64_t touched = 0;
   for (int p = first; p <= last; ++p)
     if (c->group[p] == p) {
       src.o[n] = slot_o(c, p);
       src.lse[n] = slot_lse(c, p);
+      touched |= slot_bit(c->phys[p]);
       ++n;
       if (c->stamp[p] < oldest) oldest = c->stamp[p];
     }
@@ -209,9 +264,13 @@ int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, 
     // elements of every source before it writes them.
     const dita_shape& s = c->shape;
     const int64_t rows = int64_t(s.B) * s.H * s.Nq;
-    const int st = hip_status(
+    int st = slots_wait(c, stream, touched);
+    if (st) return st;
+    st = hip_status(
         dita::launch_merge(s.dtype, s.D, rows, n, src, slot_o(c, first), slot_lse(c, first), stream));
     if (st) return st;
+    // The members' slots go back to the pool below: their next owner waits for this merge.
+    if ((st = slots_mark(c, stream, touched))) return st;
   }
   for (int p = first; p <= last; ++p) {
     c->group[p] = int16_t(first);
@@ -220,6 +279,25 @@ int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, 
     if (p != first) release(c, p);
   }
   if (launched) *launched = n > 1 ? 1 : 0;
+  return DITA_OK;
+}
+
+// Arguments of dita_state_change (and of its allocation-free variant).
+int check_change_args(const dita_shape* shape, const void* o_new, const float* lse_new,
+                      const void* o_prev, const float* lse_prev, int roll, const double* out) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_dev(o_new)) || (st = check_dev(o_prev)) || (st = check_dev(out))) return st;
+  if (roll != 0 && roll != 1) return DITA_ERR_ARG;
+  const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
+  if (overlaps(o_new, ob, o_prev, ob) || overlaps(out, 24, o_prev, ob) || overlaps(out, 24, o_new, ob))
+    return DITA_ERR_ARG;
+  if (roll) {
+    if ((st = check_dev(lse_new)) || (st = check_dev(lse_prev))) return st;
+    if (overlaps(lse_new, lb, lse_prev, lb) || overlaps(lse_prev, lb, o_new, ob) ||
+        overlaps(o_prev, ob, lse_new, lb) || overlaps(out, 24, lse_prev, lb))
+      return DITA_ERR_ARG;
+  }
   return DITA_OK;
 }
 
@@ -323,6 +401,12 @@ int cache_init(dita_state_cache** out, const dita_shape* shape, int P, int S, bo
   }
   c->ev_fork = nullptr;
   c->ev_join = nullptr;
+  for (int k = 0; k < DITA_MAX_PARTITIONS; ++k) c->slot_ev[k] = -1;
+  for (int e = 0; e <= DITA_MAX_PARTITIONS; ++e) {
+    c->ev[e] = nullptr;
+    c->ev_stream[e] = nullptr;
+    c->ev_refs[e] = 0;
+  }
   *out = c;
   return DITA_OK;
 }
@@ -344,11 +428,14 @@ int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, 
 int dita_state_cache_free(dita_state_cache* cache) {
   if (!cache) return DITA_OK;
   int st = DITA_OK;
-  for (hipEvent_t e : {cache->ev_fork, cache->ev_join})
-    if (e) {
-      const int s2 = hip_status(hipEventDestroy(e));
-      if (!st) st = s2;
-    }
+  auto destroy = [&](hipEvent_t e) {
+    if (!e) return;
+    const int s2 = hip_status(hipEventDestroy(e));
+    if (!st) st = s2;
+  };
+  destroy(cache->ev_fork);
+  destroy(cache->ev_join);
+  for (int e = 0; e <= DITA_MAX_PARTITIONS; ++e) destroy(cache->ev[e]);
   delete cache;
   return st;
 }
@@ -376,9 +463,12 @@ int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const 
   uint64_t taken = 0;
   const int k = cache->phys[p] >= 0 ? cache->phys[p] : take_free(cache, &taken);
   if (k < 0) return DITA_ERR_SIZE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = slots_wait(cache, hs, slot_bit(k)))) return st;
   st = hip_status(dita::launch_copy_state(o, lse, phys_o(cache, k), phys_lse(cache, k),
-                                          cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
+                                          cache->o_bytes, lb, hs));
   if (st) return st;
+  if ((st = slots_mark(cache, hs, slot_bit(k)))) return st;
   cache->phys[p] = int16_t(k);
   forget_host(cache, p);
   cache->valid[p] = 1;
@@ -401,8 +491,14 @@ int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* 
       return st;
     return hip_status(hipMemcpyAsync(lse, cache->host_lse[p], lb, hipMemcpyHostToDevice, hs));
   }
-  return hip_status(dita::launch_copy_state(slot_o(cache, p), slot_lse(cache, p), o, lse,
-                                            cache->o_bytes, lb, static_cast<hipStream_t>(stream)));
+  // The ordering record of a pooled slot is bookkeeping, not the cache's state.
+  dita_state_cache* mc = const_cast<dita_state_cache*>(cache);
+  const uint64_t k = slot_bit(cache->phys[p]);
+  if ((st = slots_wait(mc, hs, k))) return st;
+  if ((st = hip_status(dita::launch_copy_state(slot_o(cache, p), slot_lse(cache, p), o, lse,
+                                               cache->o_bytes, lb, hs))))
+    return st;
+  return slots_mark(mc, hs, k);
 }
 
 int dita_state_cache_invalidate(dita_state_cache* cache, int p) {
@@ -603,10 +699,30 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipStream_t side = opts ? static_cast<hipStream_t>(opts->side_stream) : nullptr;
   if (side == hs) side = nullptr;
+  if (side) {
+    // The side stream may write (o, lse) while the attention on `stream` still
+    // reads Q and the fresh K/V: none of them may share memory with the output.
+    const size_t esz = elem_size(s.dtype);
+    const size_t row_bytes = size_t(s.B) * size_t(s.H) * size_t(s.D) * esz;
+    if (overlaps(o, ob, q, ob) || overlaps(lse, lb, q, ob)) return DITA_ERR_ARG;
+    for (int p = 0; p < P; ++p) {
+      if (reuse[p]) continue;
+      const size_t kb = row_bytes * size_t(nk_list[p]);
+      if (overlaps(o, ob, k_list[p], kb) || overlaps(lse, lb, k_list[p], kb) ||
+          overlaps(o, ob, v_list[p], kb) || overlaps(lse, lb, v_list[p], kb))
+        return DITA_ERR_ARG;
+    }
+  }
   const int min_pre = opts && opts->min_premerge > 2 ? opts->min_premerge : 2;
   const bool premerge = side && n_fresh > 0 && n_reused_heads >= min_pre;
   const bool use_side = side && (premerge || n_fetch > 0);
   if (use_side && (st = ensure_events(cache))) return st;
+
+  // Pooled slots this step writes (fresh, fetched) or reads (reused leaders).
+  uint64_t touched = 0;
+  for (int p = 0; p < P; ++p)
+    if (!reuse[p] || cache->group[p] == p) touched |= slot_bit(phys[p]);
+  if ((st = slots_wait(cache, hs, touched))) return st;
 
   if (info && info->ev_begin && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_begin), hs))))
     return st;
@@ -673,6 +789,7 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     ++n_src;
   }
   if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_src, src, o, lse, hs)))) return st;
+  if ((st = slots_mark(cache, hs, touched))) return st;
   if (info && info->ev_end && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_end), hs))))
     return st;
   if (info) {
@@ -697,10 +814,14 @@ int dita_state_cache_offload(dita_state_cache* cache, int p, void* host_o, float
   if (!resident(cache, p)) return DITA_ERR_STATE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const size_t lb = state_lse_bytes(cache->shape);
+  const uint64_t k = slot_bit(cache->phys[p]);
+  if ((st = slots_wait(cache, hs, k))) return st;
   if ((st = hip_status(hipMemcpyAsync(host_o, slot_o(cache, p), cache->o_bytes,
                                       hipMemcpyDeviceToHost, hs))) ||
       (st = hip_status(hipMemcpyAsync(host_lse, slot_lse(cache, p), lb, hipMemcpyDeviceToHost, hs))))
     return st;
+  // The slot goes back to the pool: its next owner waits for these copies.
+  if ((st = slots_mark(cache, hs, k))) return st;
   cache->on_host[p] = 1;
   cache->host_o[p] = host_o;
   cache->host_lse[p] = host_lse;
@@ -716,11 +837,13 @@ int dita_state_cache_fetch(dita_state_cache* cache, int p, void* stream) {
   const int k = cache->phys[p] >= 0 ? cache->phys[p] : take_free(cache, &taken);
   if (k < 0) return DITA_ERR_SIZE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = slots_wait(cache, hs, slot_bit(k)))) return st;
   if ((st = hip_status(hipMemcpyAsync(phys_o(cache, k), cache->host_o[p], cache->o_bytes,
                                       hipMemcpyHostToDevice, hs))) ||
       (st = hip_status(hipMemcpyAsync(phys_lse(cache, k), cache->host_lse[p],
                                       state_lse_bytes(cache->shape), hipMemcpyHostToDevice, hs))))
     return st;
+  if ((st = slots_mark(cache, hs, slot_bit(k)))) return st;
   cache->phys[p] = int16_t(k);
   forget_host(cache, p);
   return DITA_OK;
@@ -765,30 +888,36 @@ int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, do
   int st;
   if ((st = check_dev(lse)) || (st = check_dev(w_out))) return st;
   const float* lses[DITA_MAX_PARTITIONS];
+  uint64_t touched = 0;
   for (int p = 0; p < cache->P; ++p) {
     if (!resident(cache, p) || group_last(cache, p) != p) return DITA_ERR_STATE;
     lses[p] = slot_lse(cache, p);
+    touched |= slot_bit(cache->phys[p]);
   }
-  return dita_state_contrib(&cache->shape, cache->P, lses, lse, w_out, stream);
+  if ((st = check_shape(&cache->shape))) return st;
+  dita_state_cache* mc = const_cast<dita_state_cache*>(cache);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = slots_wait(mc, hs, touched))) return st;
+  if ((st = dita_state_contrib(&cache->shape, cache->P, lses, lse, w_out, stream))) return st;
+  return slots_mark(mc, hs, touched);
 }
 
 int dita_state_change(const dita_shape* shape, const void* o_new, const float* lse_new,
                       void* o_prev, float* lse_prev, int roll, double* out, void* stream) {
-  int st = check_shape(shape);
+  const int st = check_change_args(shape, o_new, lse_new, o_prev, lse_prev, roll, out);
   if (st) return st;
-  if ((st = check_dev(o_new)) || (st = check_dev(o_prev)) || (st = check_dev(out))) return st;
-  if (roll != 0 && roll != 1) return DITA_ERR_ARG;
+  // Partial sums of the workgroups: stream-ordered scratch from HIP's pool,
+  // returned to it once the finishing kernel has read it.
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
-  if (overlaps(o_new, ob, o_prev, ob) || overlaps(out, 24, o_prev, ob) || overlaps(out, 24, o_new, ob))
-    return DITA_ERR_ARG;
-  if (roll) {
-    if ((st = check_dev(lse_new)) || (st = check_dev(lse_prev))) return st;
-    if (overlaps(lse_new, lb, lse_prev, lb) || overlaps(lse_prev, lb, o_new, ob) ||
-        overlaps(o_prev, ob, lse_new, lb) || overlaps(out, 24, lse_prev, lb))
-      return DITA_ERR_ARG;
-  }
-  return hip_status(dita::launch_change(shape->dtype, o_new, o_prev, ob, lse_new, lse_prev,
-                                        roll ? lb : 0, roll, out, static_cast<hipStream_t>(stream)));
+  const size_t scratch_bytes = size_t(2) * size_t(dita::change_groups(ob)) * sizeof(double);
+  void* part = nullptr;
+  int s2 = hip_status(hipMallocAsync(&part, scratch_bytes, hs));
+  if (s2) return s2;
+  s2 = hip_status(dita::launch_change(shape->dtype, o_new, o_prev, ob, lse_new, lse_prev,
+                                      roll ? lb : 0, roll, static_cast<double*>(part), out, hs));
+  const int s3 = hip_status(hipFreeAsync(part, hs));
+  return s2 ? s2 : s3;
 }
 
 int dita_planner_mask_cache(const dita_planner* planner, const dita_state_cache* cache,

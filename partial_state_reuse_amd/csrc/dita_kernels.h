@@ -55,10 +55,13 @@ hipError_t launch_contrib(int P, const LseList& src, const float* lse, int64_t r
                           hipStream_t stream);
 
 // out[0] = sum (new - prev)^2, out[1] = sum prev^2, out[2] = sqrt(out[0] / out[1]) over the
-// O elements (fp64); roll != 0 also copies the new state (O and LSE) over prev.
+// O elements (fp64, summation order fixed by o_bytes); roll != 0 also copies the new state
+// (O and LSE) over prev.  `partials` holds 2 * change_groups(o_bytes) doubles of scratch.
+constexpr int kChangeMaxGroups = 1024;
+int change_groups(size_t o_bytes);
 hipError_t launch_change(int dtype, const void* o_new, void* o_prev, size_t o_bytes,
                          const float* lse_new, float* lse_prev, size_t lse_bytes, int roll,
-                         double* out, hipStream_t stream);
+                         double* partials, double* out, hipStream_t stream);
 
 // Copy of one attention state (O bytes and LSE bytes, each a multiple of 4 bytes).
 hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,

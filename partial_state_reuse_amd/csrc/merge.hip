@@ -78,9 +78,12 @@ struct Vec<__bf16> {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// o and lse may be source 0 (in-place composition and the pre-merged two-stream
+// step), so they are not declared __restrict__: every load of a lane's chunk
+// (and of the row's LSE) feeds the lane's single store of that chunk.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows,
-                                                         T* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows, T* o,
+                                                         float* lse) {
   constexpr int VN = Vec<T>::N;
   constexpr int LPR = D / VN;          // lanes per row
   constexpr int RPB = kThreads / LPR;  // rows per block

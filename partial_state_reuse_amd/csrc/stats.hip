@@ -9,10 +9,12 @@
 //   order (deterministic).  Run at anchor steps only: at the 75,600-token
 //   shape 16 x 189,000 rows, ~12 MB.
 // change_kernel: sums of (a - b)^2 and b^2 over two output states, fp64 per
-//   lane, workgroup tree reduction, one fp64 atomic add per workgroup (the
-//   order of those adds is not fixed); optionally copies a over b (state and
-//   LSE) in the same pass.  HBM-bound: reads 2 states, writes one when rolling.
-// change_finish_kernel: ratio sqrt(sum (a-b)^2 / sum b^2).
+//   lane, a fixed-order workgroup reduction, one partial pair per workgroup
+//   into a scratch buffer; optionally copies a over b (state and LSE) in the
+//   same pass.  HBM-bound: reads 2 states, writes one when rolling.
+// change_finish_kernel: one workgroup adds the partials in a fixed order and
+//   forms the ratio sqrt(sum (a-b)^2 / sum b^2).  The grid depends only on the
+//   state's size, so the result is the same bit for bit on every run.
 
 #include "dita_kernels.h"
 
@@ -25,6 +27,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 1024;
 constexpr int kChangeThreads = 256;
+constexpr int kChangeItems = kChangeThreads * 8;  // 16-byte chunks per workgroup before the cap
 
 __device__ double block_sum(double v, double* red) {
   // wave reduction, then one value per wave through LDS
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(kChangeThreads) void change_kernel(const u32x4* __r
                                                                 u32x4* __restrict__ b, int64_t n16,
                                                                 const float* __restrict__ la,
                                                                 float* __restrict__ lb, int64_t nl,
-                                                                int roll, double* __restrict__ out) {
+                                                                int roll, double* __restrict__ part) {
   __shared__ double red[kChangeThreads / 64];
   constexpr int N = 16 / sizeof(T);
   const int64_t stride = int64_t(gridDim.x) * kChangeThreads;
@@ -105,19 +108,30 @@ __global__ __launch_bounds__(kChangeThreads) void change_kernel(const u32x4* __r
   __syncthreads();
   const double s_b = block_sum(b2, red);
   if (threadIdx.x == 0) {
-    atomicAdd(out, s_d);
-    atomicAdd(out + 1, s_b);
+    part[2 * blockIdx.x] = s_d;
+    part[2 * blockIdx.x + 1] = s_b;
   }
 }
 
-__global__ void zero3_kernel(double* out) {
-  if (threadIdx.x < 3) out[threadIdx.x] = 0.0;
-}
-
-__global__ void change_finish_kernel(double* out) {
-  if (threadIdx.x != 0) return;
-  const double num = out[0], den = out[1];
-  out[2] = den > 0.0 ? sqrt(num / den) : (num > 0.0 ? INFINITY : 0.0);
+// Thread t adds the partials of workgroups t, t + 256, ... in order; the
+// workgroup sum then runs in the fixed order of block_sum.
+__global__ __launch_bounds__(kChangeThreads) void change_finish_kernel(const double* __restrict__ part,
+                                                                       int groups,
+                                                                       double* __restrict__ out) {
+  __shared__ double red[kChangeThreads / 64];
+  double d = 0.0, b = 0.0;
+  for (int g = threadIdx.x; g < groups; g += kChangeThreads) {
+    d += part[2 * g];
+    b += part[2 * g + 1];
+  }
+  const double num = block_sum(d, red);
+  __syncthreads();
+  const double den = block_sum(b, red);
+  if (threadIdx.x == 0) {
+    out[0] = num;
+    out[1] = den;
+    out[2] = den > 0.0 ? sqrt(num / den) : (num > 0.0 ? INFINITY : 0.0);
+  }
 }
 
 }  // namespace
@@ -128,26 +142,29 @@ hipError_t launch_contrib(int P, const LseList& src, const float* lse, int64_t r
   return hipGetLastError();
 }
 
+int change_groups(size_t o_bytes) {
+  const int64_t n16 = int64_t(o_bytes / 16);
+  int64_t g = (n16 + kChangeItems - 1) / kChangeItems;
+  if (g > kChangeMaxGroups) g = kChangeMaxGroups;
+  return g < 1 ? 1 : int(g);
+}
+
 hipError_t launch_change(int dtype, const void* o_new, void* o_prev, size_t o_bytes,
                          const float* lse_new, float* lse_prev, size_t lse_bytes, int roll,
-                         double* out, hipStream_t stream) {
-  zero3_kernel<<<1, 64, 0, stream>>>(out);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                         double* partials, double* out, hipStream_t stream) {
   const int64_t n16 = int64_t(o_bytes / 16), nl = int64_t(lse_bytes / 4);
-  int64_t blocks = (n16 + kChangeThreads - 1) / kChangeThreads;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
+  const int groups = change_groups(o_bytes);
   const u32x4* a = static_cast<const u32x4*>(o_new);
   u32x4* b = static_cast<u32x4*>(o_prev);
   if (dtype == 1)
-    change_kernel<__bf16><<<dim3(unsigned(blocks)), kChangeThreads, 0, stream>>>(a, b, n16, lse_new,
-                                                                                lse_prev, nl, roll, out);
+    change_kernel<__bf16><<<dim3(unsigned(groups)), kChangeThreads, 0, stream>>>(
+        a, b, n16, lse_new, lse_prev, nl, roll, partials);
   else
-    change_kernel<float><<<dim3(unsigned(blocks)), kChangeThreads, 0, stream>>>(a, b, n16, lse_new,
-                                                                               lse_prev, nl, roll, out);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  change_finish_kernel<<<1, 64, 0, stream>>>(out);
+    change_kernel<float><<<dim3(unsigned(groups)), kChangeThreads, 0, stream>>>(
+        a, b, n16, lse_new, lse_prev, nl, roll, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  change_finish_kernel<<<1, kChangeThreads, 0, stream>>>(partials, groups, out);
   return hipGetLastError();
 }
 

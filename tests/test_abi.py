@@ -421,3 +421,88 @@ def test_event_helpers_validate():
     assert lib.dita_event_record(None, None) == dita.DITA_ERR_ARG
     assert lib.dita_event_elapsed_ms(None, None, None) == dita.DITA_ERR_ARG
     assert lib.dita_event_destroy(None) == 0
+
+
+def test_attn_step_ex_rejects_output_aliasing_inputs_with_side_stream():
+    """With a side stream, (o, lse) may not share memory with q or a fresh K/V:
+    the pre-merge would write them while the attention reads those.  Without a
+    side stream the same aliasing is accepted (validation passes up to the point
+    where the fake pointers would be used, so it is not launched here)."""
+    shape = dita.Shape(1, 2, 128, dita.DITA_BF16, 64, 0.0)
+    h = _cache(shape, 2)
+    n = lib.dita_state_cache_bytes(ctypes.byref(shape), 2)
+    base = FAKE_DEV + n + 4096
+    q = base
+    kv = [base + (1 << 20), base + (2 << 20)]
+    ks = (ctypes.c_void_p * 2)(*kv)
+    vs = (ctypes.c_void_p * 2)(base + (3 << 20), base + (4 << 20))
+    nk = (ctypes.c_int64 * 2)(64, 64)
+    fresh = (ctypes.c_uint8 * 2)(0, 0)
+    side = dita.StepOpts(FAKE_DEV + 64, 0, 0)
+    lse_ok = base + (6 << 20)
+    for o, l in [(q, lse_ok), (kv[1] + 256, lse_ok), (base + (5 << 20), q + 64),
+                 (base + (5 << 20), vs[0] + 1024)]:
+        assert lib.dita_attn_step_ex(h, q, ks, vs, nk, fresh, 0, o, l, None, ctypes.byref(side),
+                                     None) == dita.DITA_ERR_ARG
+    for p in range(2):
+        valid = ctypes.c_int()
+        lib.dita_state_cache_info(h, p, ctypes.byref(valid), None)
+        assert valid.value == 0
+    lib.dita_state_cache_free(h)
+
+
+def _no_c_calls(monkeypatch, names):
+    def boom(*a, **k):
+        raise AssertionError("the C library was called")
+    for n in names:
+        monkeypatch.setattr(dita._lib, n, boom)
+
+
+def test_binding_rejects_mismatched_tensors_before_calling(monkeypatch):
+    """Every wrapper checks shapes and dtypes against each other and against the
+    cache before it passes a pointer: a short or mistyped buffer raises ValueError
+    and nothing reaches the library."""
+    import torch
+    _no_c_calls(monkeypatch, ["dita_attn_partial", "dita_state_merge", "dita_attn_step",
+                              "dita_attn_step_ex", "dita_state_cache_store",
+                              "dita_state_cache_load", "dita_state_cache_contrib",
+                              "dita_state_contrib", "dita_state_change"])
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 2, 64, 128, dtype=bf)
+    k = torch.zeros(1, 2, 96, 128, dtype=bf)
+    bad = [
+        lambda: dita.dita_attn_partial(q, k, torch.zeros(1, 2, 95, 128, dtype=bf)),
+        lambda: dita.dita_attn_partial(q, k, k.float()),
+        lambda: dita.dita_attn_partial(q, torch.zeros(1, 2, 96, 64, dtype=bf), k),
+        lambda: dita.dita_attn_partial(q, k, k, o=torch.zeros(1, 2, 63, 128, dtype=bf)),
+        lambda: dita.dita_attn_partial(q, k, k, lse=torch.zeros(1, 2, 64, dtype=bf)),
+        lambda: dita.dita_state_merge([q, q], [torch.zeros(1, 2, 64), torch.zeros(1, 2, 64)],
+                                      o=torch.zeros(1, 2, 64, 64, dtype=bf)),
+        lambda: dita.dita_state_merge([q, q[:, :1]], [torch.zeros(1, 2, 64)] * 2),
+        lambda: dita.dita_state_contrib([torch.zeros(1, 2, 64)], torch.zeros(1, 2, 64),
+                                        w=torch.zeros(2, dtype=torch.float64)),
+        lambda: dita.dita_state_change(q, q[:, :, :32]),
+        lambda: dita.dita_state_change(q, q, out=torch.zeros(2, dtype=torch.float64)),
+        lambda: dita.dita_state_change(q, q, roll=True),
+    ]
+    cache = dita.StateCache(1, 2, 64, 128, bf, P=2, device="cpu")
+    lse = torch.zeros(1, 2, 64, dtype=f32)
+    bad += [
+        lambda: cache.store(0, q[:, :, :32], lse, step=0),
+        lambda: cache.store(0, q.float(), lse, step=0),
+        lambda: cache.store(0, q, lse[:, :1], step=0),
+        lambda: cache.load(0, o=q.float()),
+        lambda: cache.contrib(lse.double()),
+        lambda: dita.dita_attn_step(cache, q[:, :1], [k, k], [k, k], [0, 0], 0),
+        lambda: dita.dita_attn_step(cache, q, [k, k], [k, k[:, :, :50]], [0, 0], 0),
+        lambda: dita.dita_attn_step(cache, q, [k, None], [k, k], [0, 0], 0),
+        lambda: dita.dita_attn_step(cache, q, [k, k.float()], [k, k.float()], [0, 0], 0),
+        lambda: dita.dita_attn_step(cache, q, [k, torch.zeros(1, 2, 96, 64, dtype=bf)],
+                                    [k, torch.zeros(1, 2, 96, 64, dtype=bf)], [0, 0], 0),
+        lambda: dita.dita_attn_step(cache, q, [k, k], [k, k], [0, 0], 0, o=q.float()),
+        lambda: dita.dita_attn_step(cache, q, [k, k], [k, k], [0, 0], 0, lse=lse[:, :, :10]),
+    ]
+    for i, fn in enumerate(bad):
+        with pytest.raises(ValueError):
+            fn()
+    cache.close()

@@ -224,3 +224,79 @@ def test_sixty_four_partitions_with_groups_and_offload(dev):
                 if ref.group_range(p)[1] > p:
                     cache.offload(p)
             assert cache.residency()[1] == sum(1 for p in ref.leaders() if ref.group_range(p)[1] > p)
+
+
+def _random_state(rng, H, nq, D):
+    o = round_bf16(rng.standard_normal((1, H, nq, D)) * 0.7)
+    lse = (rng.standard_normal((1, H, nq)) + 6.0).astype(np.float32)
+    return o, lse
+
+
+def test_pooled_slot_released_on_one_stream_taken_on_another(dev):
+    """Offload on stream A frees a pooled slot; a step on stream B fetches the state
+    back into that slot and reuses the other, which A stored.  Stream A is held
+    back first by a bounded sleep kernel, so B's work would run ahead of A's
+    copies if the library did not order the slots: the result must still be the
+    oracle's merge of the two stored states, and the host copy exact."""
+    import torch
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(36)
+    H, nq, D, P = 16, 2048, 128, 2
+    x0, x1 = _random_state(rng, H, nq, D), _random_state(rng, H, nq, D)
+    a, b = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=2)
+    d0 = (to_dev(x0[0], "bf16", dev), torch.from_numpy(x0[1]).to(dev))
+    d1 = (to_dev(x1[0], "bf16", dev), torch.from_numpy(x1[1]).to(dev))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(a):
+        torch.cuda._sleep(20_000_000)               # ~10 ms, bounded
+    cache.store(0, *d0, step=0, stream=a)
+    cache.store(1, *d1, step=0, stream=a)
+    ho, hl = cache.offload(1, stream=a)
+    assert cache.residency() == (1, 1, 1)
+    q = to_dev(np.zeros((1, H, nq, D), np.float32), "bf16", dev)
+    o, lse, info = dita.dita_attn_step(cache, q, [None, None], [None, None],
+                                       np.ones(P, np.uint8), 1, stream=b)
+    assert info.fetched == 1
+    torch.cuda.synchronize()
+    assert np.array_equal(ho.float().numpy(), x1[0]) and np.array_equal(hl.numpy(), x1[1])
+    ref = OracleCache(P)
+    ref.store(0, x0, 0)
+    ref.store(1, x1, 0)
+    o_ref, lse_ref, _ = oracle_step(ref, None, [None, None], [None, None], np.ones(P, np.uint8), 1)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "two-stream pooled fetch")
+
+
+def test_pooled_slot_freed_by_compose_then_written_on_another_stream(dev):
+    """Composition on stream A frees a member's pooled slot; a step on stream B
+    recomputes the group, so its attention writes that slot and the leader's.
+    With A held back by a bounded sleep, only the library's ordering keeps B from
+    writing before A's in-place merge has read and written them."""
+    import torch
+    import partial_state_reuse_amd as dita
+    rng = np.random.default_rng(37)
+    H, nq, D, P = 8, 1024, 128, 3
+    lengths = [300, 200, 250]
+    q, ks, vs = _inputs(rng, H, nq, lengths, D)
+    xs = [_random_state(rng, H, nq, D) for _ in range(P)]
+    a, b = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=3)
+    dx = [(to_dev(x[0], "bf16", dev), torch.from_numpy(x[1]).to(dev)) for x in xs]
+    qd, kd, vd = to_dev(q, "bf16", dev), _dev(ks, dev), _dev(vs, dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(a):
+        torch.cuda._sleep(20_000_000)
+    for p in range(P):
+        cache.store(p, *dx[p], step=0, stream=a)
+    cache.compose(0, 1, stream=a)
+    assert cache.residency() == (2, 0, 1)
+    mask = np.array([0, 0, 1], np.uint8)
+    o, lse, info = dita.dita_attn_step(cache, qd, kd, vd, mask, 1, stream=b)
+    assert info.n_fresh == 2
+    torch.cuda.synchronize()
+    ref = OracleCache(P)
+    for p in range(P):
+        ref.store(p, xs[p], 0)
+    ref.compose(0, 1)
+    o_ref, lse_ref, _ = oracle_step(ref, q, ks, vs, mask, 1)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "two-stream pooled compose")

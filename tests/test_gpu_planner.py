@@ -129,3 +129,62 @@ def test_error_planned_schedule_matches_oracle(dev):
             ref_pl.observe(s, d)
         say(f"[error planner] step {s}: fresh {nf}/{P}  mask {''.join(map(str, mask))}")
     assert reused_total > 0
+
+
+def test_state_change_is_bitwise_reproducible(dev):
+    """The change statistic sums in an order fixed by the state's size alone: the
+    same inputs give the same three doubles bit for bit, at the 75,600-token
+    state's size (many workgroups, capped grid)."""
+    import torch
+    import partial_state_reuse_amd as dita
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    shape = (1, 40, 4725, 128)
+    a = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    b = (a.float() + 0.03 * torch.randn(shape, generator=g, device=dev)).to(torch.bfloat16)
+    outs = [dita.dita_state_change(a, b).clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert bool((o == outs[0]).all()), (outs[0], o)
+    ref = float(((a.double() - b.double()) ** 2).sum() / (b.double() ** 2).sum()) ** 0.5
+    assert to_host(outs[0])[2] == pytest.approx(ref, rel=1e-12)
+
+
+def test_error_planned_schedule_is_reproducible(dev):
+    """Two runs of an error-planned schedule, the planner fed by the library's own
+    statistics kernels: identical measured changes and identical masks."""
+    import torch
+    import partial_state_reuse_amd as dita
+    wl = workloads.reduced("dit75k_ramp50", H=4, grid=(21, 15, 16), steps=12)
+    P, q = wl.P, wl.q_part
+    inp = Inputs(wl, seed=4)
+    tdt = torch.bfloat16
+    q_dev = to_dev(inp.q, "bf16", dev)
+    kv = []
+    for s in range(wl.steps):
+        k, v = inp.kv(s)
+        kv.append(([to_dev(np.ascontiguousarray(x), "bf16", dev) for x in split_parts(k, wl)],
+                   [to_dev(np.ascontiguousarray(x), "bf16", dev) for x in split_parts(v, wl)]))
+    runs = []
+    for run in range(2):
+        cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, P, device=dev)
+        planner = dita.ErrorPlanner(P, q, 2, 0.004, 6)
+        prev_o = torch.zeros((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
+        prev_l = torch.zeros((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+        masks, deltas = [], []
+        for s in range(wl.steps):
+            mask, _ = planner.mask(s, cache=cache)
+            _, lse, info = dita.dita_attn_step(cache, q_dev, kv[s][0], kv[s][1], mask, s)
+            if info.n_fresh == P:
+                planner.set_weights(list(to_host(cache.contrib(lse))))
+            so, sl = cache.slot(q)
+            out = dita.dita_state_change(so, prev_o, sl, prev_l, roll=True)
+            if s > 0:
+                d = float(to_host(out)[2])
+                planner.observe(s, d)
+                deltas.append(d)
+            masks.append(mask.copy())
+        runs.append((masks, deltas))
+        say(f"[reproducible planner] run {run}: deltas {deltas[:3]} ...")
+    assert all(np.array_equal(x, y) for x, y in zip(runs[0][0], runs[1][0]))
+    assert runs[0][1] == runs[1][1]
