@@ -437,6 +437,22 @@ int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, do
 int dita_state_change(const dita_shape* shape, const void* o_new, const float* lse_new,
                       void* o_prev, float* lse_prev, int roll, double* out, void* stream);
 
+/*
+ * dita_state_change_noalloc -- dita_state_change for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, same kernels, same
+ * result bit for bit; no hipMalloc, hipMallocAsync or hipFree.  The partial
+ * sums live in a 16 KB array in the library's own device memory (one copy per
+ * GPU, kept until the process ends; its address is looked up once per device
+ * with hipGetSymbolAddress).  That array covers every state size (the grid is
+ * capped at 1024 workgroups); DITA_ERR_SIZE would mean a grid beyond it.  All
+ * calls on one GPU share the array and nothing in it needs clearing (each
+ * call writes every partial it reads), so calls that overlap on one GPU --
+ * on different streams, or from different threads without ordering -- race
+ * and may return wrong sums: serialise them.
+ */
+int dita_state_change_noalloc(const dita_shape* shape, const void* o_new, const float* lse_new,
+                              void* o_prev, float* lse_prev, int roll, double* out, void* stream);
 
 /*
  * Error-guided planner (host only, float64).  Page section: 1. Anchor-Guided

@@ -127,6 +127,7 @@ def _load() -> ctypes.CDLL:
         "dita_state_contrib": (i32, [ctypes.POINTER(Shape), i32, pvp, vp, vp, vp]),
         "dita_state_cache_contrib": (i32, [vp, vp, vp, vp]),
         "dita_state_change": (i32, [ctypes.POINTER(Shape), vp, vp, vp, vp, i32, vp, vp]),
+        "dita_state_change_noalloc": (i32, [ctypes.POINTER(Shape), vp, vp, vp, vp, i32, vp, vp]),
         "dita_planner_create": (i32, [pvp, ctypes.POINTER(ErrorPlan)]),
         "dita_planner_free": (i32, [vp]),
         "dita_planner_set_weights": (i32, [vp, ctypes.POINTER(ctypes.c_double)]),
@@ -574,6 +575,29 @@ def dita_state_change(o_new, o_prev, lse_new=None, lse_prev=None, roll: bool = F
     _check(_lib.dita_state_change(ctypes.byref(shape), _ptr(o_new), _ptr(lse_new), _ptr(o_prev),
                                   _ptr(lse_prev), int(bool(roll)), _ptr(out), _stream(o_new, stream)),
            "dita_state_change")
+    return out
+
+
+def dita_state_change_noalloc(o_new, o_prev, out, lse_new=None, lse_prev=None,
+                              roll: bool = False, stream=None):
+    """dita_state_change without any device allocation: the caller passes ``out``
+    (float64 [3]); the library's fixed device scratch holds the partial sums, so
+    calls that overlap on one GPU race."""
+    torch = _torch()
+    if o_new.dim() != 4:
+        raise ValueError(f"states must be [B, H, Nq, D], got shape {tuple(o_new.shape)}")
+    _expect(o_prev, o_new.shape, o_new.dtype, "o_prev")
+    if roll and (lse_new is None or lse_prev is None):
+        raise ValueError("rolling needs lse_new and lse_prev")
+    for t, name in ((lse_new, "lse_new"), (lse_prev, "lse_prev")):
+        if t is not None:
+            _expect(t, o_new.shape[:3], torch.float32, name)
+    _expect(out, (3,), torch.float64, "out")
+    _same_device("dita_state_change_noalloc", o_new, o_prev, lse_new, lse_prev, out)
+    shape = make_shape(o_new)
+    _check(_lib.dita_state_change_noalloc(ctypes.byref(shape), _ptr(o_new), _ptr(lse_new),
+                                          _ptr(o_prev), _ptr(lse_prev), int(bool(roll)), _ptr(out),
+                                          _stream(o_new, stream)), "dita_state_change_noalloc")
     return out
 
 

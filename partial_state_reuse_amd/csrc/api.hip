@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/dita.h"
@@ -918,6 +919,56 @@ int dita_state_change(const dita_shape* shape, const void* o_new, const float* l
                                       roll ? lb : 0, roll, static_cast<double*>(part), out, hs));
   const int s3 = hip_status(hipFreeAsync(part, hs));
   return s2 ? s2 : s3;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of dita_state_change_noalloc: the partial sums of the change
+// statistic's workgroups (two doubles each; the grid never exceeds
+// dita::kChangeMaxGroups workgroups, so 16 KB covers every state size).  Each
+// GPU holds its own copy until the process ends; host code reaches it only
+// through the per-device address from hipGetSymbolAddress.
+constexpr int kNoAllocScratchDoubles = 2 * dita::kChangeMaxGroups;
+static __device__ __align__(256) double scratch[kNoAllocScratchDoubles];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+int scratch_on_current_device(double** out) {
+  int dev = 0;
+  int st = hip_status(hipGetDevice(&dev));
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return DITA_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))))) return st;
+    if (!ptr) return DITA_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<double*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return DITA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dita_state_change_noalloc(const dita_shape* shape, const void* o_new, const float* lse_new,
+                              void* o_prev, float* lse_prev, int roll, double* out, void* stream) {
+  int st = check_change_args(shape, o_new, lse_new, o_prev, lse_prev, roll, out);
+  if (st) return st;
+  const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
+  if (2 * dita::change_groups(ob) > kNoAllocScratchDoubles) return DITA_ERR_SIZE;
+  double* part = nullptr;
+  if ((st = scratch_on_current_device(&part))) return st;
+  return hip_status(dita::launch_change(shape->dtype, o_new, o_prev, ob, lse_new, lse_prev,
+                                        roll ? lb : 0, roll, part, out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int dita_planner_mask_cache(const dita_planner* planner, const dita_state_cache* cache,
