@@ -27,6 +27,9 @@ planner    the reuse-mask planner and its SplitMix64 integer generator.
 error_planner  contribution weights, local state change and the group-wise,
            error-budgeted planner ("Error Modeling", "Online Prediction",
            "Group-wise Strategy" of the planner section).
+compress   the compact (int8 codes, per-row scale) encoding of a cached
+           state ("Significance and Claims": memory held by cached states,
+           cache compression as future work).
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against
 closed forms, textbook/library routines it does not itself call (scipy's
@@ -38,6 +41,7 @@ which the pages give no numbers for.
 
 from .attention import full_attention, merge_states, partial_state, softmax_scale
 from .cache import StateCache, attn_step, compose_runs, effective_reuse
+from .compress import compact_state, decode_rows, encode_rows
 from .error_planner import ErrorPlanner, contributions, state_change
 from .planner import (
     POLICY_DIST,
@@ -59,6 +63,9 @@ __all__ = [
     "attn_step",
     "effective_reuse",
     "compose_runs",
+    "encode_rows",
+    "decode_rows",
+    "compact_state",
     "ErrorPlanner",
     "contributions",
     "state_change",

@@ -32,6 +32,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 from .attention import State, merge_states, partial_state
+from .compress import compact_state
 
 
 @dataclass
@@ -88,6 +89,14 @@ class StateCache:
             self.valid[i] = 0
             self.stamp[i] = -1
             self.group[i] = i
+
+    def compact(self, p: int) -> None:
+        """Hold group leader p's state in the compact encoding (see compress.py):
+        from now on its output is the decoded int8 codes times the row scales,
+        its LSE unchanged.  A later store (a fresh state) replaces it."""
+        if self.group[p] != p or not self.valid[p]:
+            raise RuntimeError(f"partition {p} does not lead a group holding a state")
+        self.slots[p] = compact_state(self.slots[p])
 
     def dissolve(self, first: int) -> None:
         """Forget a group: its members become single, empty slots."""

@@ -26,13 +26,29 @@ import pytest
 ROOT = pathlib.Path(__file__).resolve().parents[1]
 PINS = {
     "attention.py": ["test_oracle_attention", "test_oracle_merge"],
-    "cache.py": ["test_oracle_merge", "test_oracle_groups"],
+    "cache.py": ["test_oracle_merge", "test_oracle_groups", "test_oracle_compress"],
+    "compress.py": ["test_oracle_compress"],
     "planner.py": ["test_oracle_planner", "test_abi"],
     "error_planner.py": ["test_oracle_error_planner", "test_abi"],
 }
 
 # (file, what the mistake is, text in the oracle, replacement)
 MUTATIONS = [
+    ("compress.py", "scale a/128", "a / np.float32(CODE_MAX)", "a / np.float32(128)"),
+    ("compress.py", "codes truncated instead of rounded", "q = np.rint(t / safe[..., None])",
+     "q = np.trunc(t / safe[..., None])"),
+    ("compress.py", "ties rounded away from zero", "q = np.rint(t / safe[..., None])",
+     "q = np.trunc(t / safe[..., None] + np.copysign(np.float32(0.5), t))"),
+    ("compress.py", "row maximum without the magnitude", "a = np.max(np.abs(x), axis=-1)",
+     "a = np.max(x, axis=-1)"),
+    ("compress.py", "codes scaled to 126", "t = x * np.float32(CODE_MAX)",
+     "t = x * np.float32(CODE_MAX - 1)"),
+    ("compress.py", "decode divides by the scale", "(c * s[..., None])", "(c / np.where(s > 0, s, 1)[..., None])"),
+    ("compress.py", "encoding the unrounded state",
+     "encode_rows(bf16_round(np.asarray(o, dtype=np.float64)))",
+     "encode_rows(np.asarray(o, dtype=np.float64).astype(np.float32))"),
+    ("cache.py", "compaction not kept", "self.slots[p] = compact_state(self.slots[p])",
+     "compact_state(self.slots[p])"),
     ("attention.py", "default scale 1/D", "1.0 / math.sqrt(head_dim)", "1.0 / head_dim"),
     ("attention.py", "scores against V instead of K",
      "s = scale * np.matmul(q, np.swapaxes(k, -1, -2))",
