@@ -394,25 +394,32 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
       mx[qb] = m;
     }
   };
+  // Eight exponentials against the running max (bf16 copies for P V) and
+  // their fp32 sum as a pairwise tree (depth 3 instead of a chain of 8).
+  auto exp8 = [&](const f32x16& s, int h2, float m, bf16x8& v) -> float {
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + j], scale_log2, -m));
+      v[j] = (__bf16)e[j];
+    }
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  };
+  // Sum of the exponentials of one query block's 16 x NB scores of this lane.
+  auto exp_block = [&](int qb, const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) -> float {
+    float part = exp8(s[qb][0], 0, m_run[qb], pb[qb][0][0]);
+    part += exp8(s[qb][0], 1, m_run[qb], pb[qb][0][1]);
+#pragma unroll
+    for (int b = 1; b < NB; ++b) {
+      part += exp8(s[qb][b], 0, m_run[qb], pb[qb][b][0]);
+      part += exp8(s[qb][b], 1, m_run[qb], pb[qb][b][1]);
+    }
+    return part;
+  };
   // Exponentials of one query block against the running max, fp32 sum into
   // the lane's partial denominator, bf16 copies for P V.
   auto softmax_qb = [&](int qb, const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 v;
-        float part = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + j], scale_log2, -m_run[qb]));
-          part += e;
-          v[j] = (__bf16)e;
-        }
-        l_run[qb] += part;
-        pb[qb][b][h2] = v;
-      }
+    l_run[qb] += exp_block(qb, s, pb);
   };
   auto softmax = [&](const f32x16 (*s)[NB], bf16x8 (*pb)[NB][2]) {
 #pragma unroll
@@ -445,23 +452,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       between(qb);
-      part[qb] = 0.0f;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          bf16x8 v;
-          float p2 = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float e =
-                __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + j], scale_log2, -m_run[qb]));
-            p2 += e;
-            v[j] = (__bf16)e;
-          }
-          part[qb] += p2;
-          pb[qb][b][h2] = v;
-        }
+      part[qb] = exp_block(qb, s, pb);
     }
     bool ok = true;
 #pragma unroll
