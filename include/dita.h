@@ -204,6 +204,55 @@ int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, 
 int dita_state_cache_offload(dita_state_cache* cache, int p, void* host_o, float* host_lse,
                              void* stream);
 
+/*
+ * Compact states.  Page section: Significance and Claims (the memory held by
+ * cached states is the method's stated limitation; cache compression is its
+ * future work).  The page gives no format; this one keeps a bf16 state's
+ * output as int8 codes with one float32 scale per row (row = one query of one
+ * head), the LSE exactly:
+ *   a = max_d |O[r, d]|;  scale[r] = a / 127;
+ *   code[r, d] = round-half-even(O[r, d] * 127 / a) in [-127, 127]
+ * (a row of zeros: scale 0, codes 0), each a float32 operation rounded once,
+ * so the encoding is reproducible bit for bit.  A merge uses code * scale
+ * (one float32 product), within scale/2 = a/254 of the stored bf16 value.
+ * Bytes per row: D + 8 against 2D + 4 (136 against 260 at D = 128).
+ *
+ * A compact cache is a pooled cache (see dita_state_cache_init_pool) with S
+ * full and C compact physical slots in one buffer of
+ * dita_state_cache_bytes_compact(shape, S, C) bytes; bf16 only
+ * (DITA_ERR_DTYPE otherwise), 1 <= S <= P, 0 <= C <= P, S + C <= 64.  Layout:
+ * the S full slots as in dita_state_cache_bytes(shape, S), then C compact
+ * slots, each int8 codes [B, H, Nq, D], float32 scales [B, H, Nq] and float32
+ * LSE [B, H, Nq], every part at a 256-byte aligned offset.
+ *
+ * dita_state_cache_compact: encode group leader p's state (held in a full
+ *   device slot) into a free compact slot and return the full slot to the
+ *   pool (DITA_ERR_SIZE if no compact slot is free; DITA_ERR_STATE if p holds
+ *   no full device state or the cache has no compact slots).  Stream-ordered;
+ *   reads 2D + 4 bytes and writes D + 8 bytes per row.
+ * A compact state is used as it is: steps that reuse it and compositions
+ * that include it read its codes and scales in the merge (a composition's
+ * result is a full state, written in place into a member's full slot, or into
+ * a free one -- DITA_ERR_SIZE, before any launch, if none); a step that
+ * recomputes it, or a store, replaces it with a full state and frees the
+ * compact slot.  dita_state_cache_load, _offload and _slot return
+ * DITA_ERR_STATE for a compact state; dita_state_cache_compact_slot gives its
+ * device parts.  Residency counts compact states as on the device; the free
+ * slots it reports are full ones.
+ */
+size_t dita_state_cache_bytes_compact(const dita_shape* shape, int S, int C);
+int dita_state_cache_init_compact(dita_state_cache** out, const dita_shape* shape, int P, int S,
+                                  int C, void* dev_buf, size_t bytes);
+int dita_state_cache_compact(dita_state_cache* cache, int p, void* stream);
+/* Device parts of p's compact state (any output pointer may be NULL); DITA_ERR_STATE unless
+ * p's state is compact.  codes: int8 [B, H, Nq, D]; scale, lse: float32 [B, H, Nq]. */
+int dita_state_cache_compact_slot(const dita_state_cache* cache, int p, void** codes, float** scale,
+                                  float** lse);
+/* Where partition p's own state is: DITA_STATE_NONE (invalid, or a member other than its
+ * group's leader), _FULL (a full device slot), _COMPACT, or _HOST. */
+enum { DITA_STATE_NONE = 0, DITA_STATE_FULL = 1, DITA_STATE_COMPACT = 2, DITA_STATE_HOST = 3 };
+int dita_state_cache_format(const dita_state_cache* cache, int p, int* format);
+
 /* Copy an offloaded state back into a device slot (DITA_ERR_SIZE if none is free). */
 int dita_state_cache_fetch(dita_state_cache* cache, int p, void* stream);
 

@@ -32,6 +32,7 @@ DITA_OK, DITA_ERR_ARG, DITA_ERR_SHAPE, DITA_ERR_DTYPE = 0, 1, 2, 3
 DITA_ERR_STATE, DITA_ERR_ALIGN, DITA_ERR_HIP, DITA_ERR_SIZE = 4, 5, 6, 7
 DITA_F32, DITA_BF16 = 0, 1
 DITA_PLAN_DIST, DITA_PLAN_KNEAREST, DITA_PLAN_RANDOM, DITA_PLAN_RAMP = 0, 1, 2, 3
+DITA_STATE_NONE, DITA_STATE_FULL, DITA_STATE_COMPACT, DITA_STATE_HOST = 0, 1, 2, 3
 MAX_PARTITIONS = 64
 
 
@@ -96,6 +97,11 @@ def _load() -> ctypes.CDLL:
         "dita_state_cache_bytes": (sz, [ctypes.POINTER(Shape), i32]),
         "dita_state_cache_init": (i32, [pvp, ctypes.POINTER(Shape), i32, vp, sz]),
         "dita_state_cache_init_pool": (i32, [pvp, ctypes.POINTER(Shape), i32, i32, vp, sz]),
+        "dita_state_cache_bytes_compact": (sz, [ctypes.POINTER(Shape), i32, i32]),
+        "dita_state_cache_init_compact": (i32, [pvp, ctypes.POINTER(Shape), i32, i32, i32, vp, sz]),
+        "dita_state_cache_compact": (i32, [vp, i32, vp]),
+        "dita_state_cache_compact_slot": (i32, [vp, i32, pvp, pvp, pvp]),
+        "dita_state_cache_format": (i32, [vp, i32, ctypes.POINTER(ctypes.c_int)]),
         "dita_state_cache_offload": (i32, [vp, i32, vp, vp, vp]),
         "dita_state_cache_fetch": (i32, [vp, i32, vp]),
         "dita_state_cache_residency": (i32, [vp, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
@@ -311,7 +317,7 @@ class StateCache:
     """
 
     def __init__(self, B: int, H: int, Nq: int, D: int, dtype, P: int, device="cuda",
-                 scale: float = 0.0, slots: Optional[int] = None):
+                 scale: float = 0.0, slots: Optional[int] = None, compact_slots: int = 0):
         torch = _torch()
         code = DITA_BF16 if dtype == torch.bfloat16 else DITA_F32 if dtype == torch.float32 else None
         if code is None:
@@ -320,22 +326,33 @@ class StateCache:
         self.P = P
         self.dtype = dtype
         self.slots = P if slots is None else int(slots)
-        nbytes = _lib.dita_state_cache_bytes(ctypes.byref(self.shape), self.slots)
+        self.compact_slots = int(compact_slots)
+        pooled = slots is not None or self.compact_slots > 0
+        if self.compact_slots > 0:
+            nbytes = _lib.dita_state_cache_bytes_compact(ctypes.byref(self.shape), self.slots,
+                                                         self.compact_slots)
+        else:
+            nbytes = _lib.dita_state_cache_bytes(ctypes.byref(self.shape), self.slots)
         if nbytes == 0:
             raise ValueError("invalid cache shape or slot count")
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
         h = ctypes.c_void_p()
-        if slots is None:
-            _check(_lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(self.shape), P,
-                                              self.buffer.data_ptr(), nbytes), "dita_state_cache_init")
-        else:
+        if self.compact_slots > 0:
+            _check(_lib.dita_state_cache_init_compact(ctypes.byref(h), ctypes.byref(self.shape), P,
+                                                      self.slots, self.compact_slots,
+                                                      self.buffer.data_ptr(), nbytes),
+                   "dita_state_cache_init_compact")
+        elif pooled:
             _check(_lib.dita_state_cache_init_pool(ctypes.byref(h), ctypes.byref(self.shape), P,
                                                    self.slots, self.buffer.data_ptr(), nbytes),
                    "dita_state_cache_init_pool")
+        else:
+            _check(_lib.dita_state_cache_init(ctypes.byref(h), ctypes.byref(self.shape), P,
+                                              self.buffer.data_ptr(), nbytes), "dita_state_cache_init")
         self.handle = h.value
         self._host = {}
         # partition p owns slot p unless the cache is pooled: the views never change
-        self._views = None if slots is not None else [self._slot_views(p) for p in range(P)]
+        self._views = None if pooled else [self._slot_views(p) for p in range(P)]
 
     def _slot_views(self, p: int):
         torch = _torch()
@@ -365,6 +382,34 @@ class StateCache:
     def slot(self, p: int):
         """Views (O_p, LSE_p) of the device memory of partition p's slot."""
         return self._views[p] if self._views is not None else self._slot_views(p)
+
+    def compact(self, p: int, stream=None):
+        """Encode leader p's full state into a compact slot (int8 codes, per-row scale)."""
+        _check(_lib.dita_state_cache_compact(self.handle, p, _stream(self.buffer, stream)),
+               "dita_state_cache_compact")
+
+    def compact_slot(self, p: int):
+        """Views (codes int8 [B,H,Nq,D], scale float32 [B,H,Nq], LSE float32 [B,H,Nq]) of
+        p's compact state."""
+        torch = _torch()
+        c, sc, l = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        _check(_lib.dita_state_cache_compact_slot(self.handle, p, ctypes.byref(c), ctypes.byref(sc),
+                                                  ctypes.byref(l)), "dita_state_cache_compact_slot")
+        s = self.shape
+        base = self.buffer.data_ptr()
+        n = s.B * s.H * s.Nq
+
+        def view(ptr, nbytes):
+            return self.buffer[ptr - base: ptr - base + nbytes]
+        return (view(c.value, n * s.D).view(torch.int8).view(s.B, s.H, s.Nq, s.D),
+                view(sc.value, n * 4).view(torch.float32).view(s.B, s.H, s.Nq),
+                view(l.value, n * 4).view(torch.float32).view(s.B, s.H, s.Nq))
+
+    def format(self, p: int) -> int:
+        """DITA_STATE_NONE, _FULL, _COMPACT or _HOST for partition p's own state."""
+        f = ctypes.c_int()
+        _check(_lib.dita_state_cache_format(self.handle, p, ctypes.byref(f)), "dita_state_cache_format")
+        return f.value
 
     def offload(self, p: int, stream=None):
         """Move leader p's state to pinned host memory (copies on ``stream``)."""

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdita.so")
 
-HIP_SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "stats.hip"]
+HIP_SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "compact.hip", "merge.hip", "stats.hip"]
 CXX_SOURCES = ["planner.cpp", "error_planner.cpp"]
 ARCH = "gfx950"
 

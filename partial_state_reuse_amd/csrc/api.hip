@@ -40,9 +40,16 @@ struct dita_state_cache {
   int16_t group[DITA_MAX_PARTITIONS];  // leader (first partition) of p's group
   hipEvent_t ev_fork;                  // stream -> side stream, created on first use
   hipEvent_t ev_join;                  // side stream -> stream
-  int S;                               // physical slots in the buffer
+  int S;                               // physical (full) slots in the buffer
   bool pool;                           // slots assigned on demand; else partition p owns slot p
   int16_t phys[DITA_MAX_PARTITIONS];   // physical slot holding p's own state, -1 if none
+  // Compact slots (int8 codes + per-row scale + LSE), after the S full slots;
+  // a state is held in a full slot, a compact slot or host memory, never two.
+  int C;
+  size_t c_base;                       // offset of compact slot 0
+  size_t c_scale_off, c_lse_off;       // offsets of the scales and the LSE inside one
+  size_t c_stride;                     // bytes per compact slot
+  int16_t cphys[DITA_MAX_PARTITIONS];  // compact slot holding p's state, -1 if none
   uint8_t on_host[DITA_MAX_PARTITIONS];  // p's state lives in caller host memory
   void* host_o[DITA_MAX_PARTITIONS];
   float* host_lse[DITA_MAX_PARTITIONS];
@@ -137,9 +144,42 @@ float* phys_lse(const dita_state_cache* c, int k) {
 void* slot_o(const dita_state_cache* c, int p) { return phys_o(c, c->phys[p]); }
 float* slot_lse(const dita_state_cache* c, int p) { return phys_lse(c, c->phys[p]); }
 
-// A state that is valid, leads its group and sits in device memory.
+char* cslot(const dita_state_cache* c, int j) { return c->base + c->c_base + size_t(j) * c->c_stride; }
+int8_t* cslot_codes(const dita_state_cache* c, int j) { return reinterpret_cast<int8_t*>(cslot(c, j)); }
+float* cslot_scale(const dita_state_cache* c, int j) {
+  return reinterpret_cast<float*>(cslot(c, j) + c->c_scale_off);
+}
+float* cslot_lse(const dita_state_cache* c, int j) {
+  return reinterpret_cast<float*>(cslot(c, j) + c->c_lse_off);
+}
+
+// A state that is valid, leads its group and sits in a full device slot.
 bool resident(const dita_state_cache* c, int p) {
   return c->valid[p] && c->group[p] == p && c->phys[p] >= 0 && !c->on_host[p];
+}
+// ... or in a full or compact device slot.
+bool on_device(const dita_state_cache* c, int p) {
+  return c->valid[p] && c->group[p] == p && !c->on_host[p] && (c->phys[p] >= 0 || c->cphys[p] >= 0);
+}
+
+// The device LSE of a leader on the device.
+const float* state_lse(const dita_state_cache* c, int p) {
+  return c->cphys[p] >= 0 ? cslot_lse(c, c->cphys[p]) : slot_lse(c, p);
+}
+
+// Append leader p's device state (either format) to a merge's sources.
+void add_source(const dita_state_cache* c, dita::MergeSrc& src, int& n, int p) {
+  if (c->cphys[p] >= 0) {
+    const int j = c->cphys[p];
+    src.o[n] = cslot_codes(c, j);
+    src.lse[n] = cslot_lse(c, j);
+    src.scale[n] = cslot_scale(c, j);
+  } else {
+    src.o[n] = slot_o(c, p);
+    src.lse[n] = slot_lse(c, p);
+    src.scale[n] = nullptr;
+  }
+  ++n;
 }
 
 // Lowest physical slot that no partition holds and `taken` does not mark; marks it.
@@ -155,9 +195,20 @@ int take_free(const dita_state_cache* c, uint64_t* taken) {
   return -1;
 }
 
+// Lowest compact slot that no partition holds; -1 if none.
+int take_free_compact(const dita_state_cache* c) {
+  uint64_t used = 0;
+  for (int p = 0; p < c->P; ++p)
+    if (c->cphys[p] >= 0) used |= uint64_t(1) << c->cphys[p];
+  for (int j = 0; j < c->C; ++j)
+    if (!((used >> j) & 1)) return j;
+  return -1;
+}
+
 // In a pooled cache a partition without a state of its own holds no slot.
 void release(dita_state_cache* c, int p) {
   if (c->pool) c->phys[p] = -1;
+  c->cphys[p] = -1;
 }
 
 void forget_host(dita_state_cache* c, int p) {
@@ -212,7 +263,7 @@ int effective_mask(const dita_state_cache* c, const uint8_t* reuse, uint8_t* out
 int slots_wait(dita_state_cache* c, hipStream_t s, uint64_t slots) {
   if (!c->pool) return DITA_OK;
   uint64_t waited = 0;
-  for (int k = 0; k < c->S; ++k) {
+  for (int k = 0; k < c->S + c->C; ++k) {
     if (!((slots >> k) & 1)) continue;
     const int e = c->slot_ev[k];
     if (e < 0 || ((waited >> e) & 1) || c->ev_stream[e] == static_cast<void*>(s)) continue;
@@ -225,7 +276,7 @@ int slots_wait(dita_state_cache* c, hipStream_t s, uint64_t slots) {
 
 int slots_mark(dita_state_cache* c, hipStream_t s, uint64_t slots) {
   if (!c->pool || !slots) return DITA_OK;
-  // A free event: at most S are referenced by slots, and there are S + 1.
+  // A free event: at most S + C <= 64 are referenced by slots, and there are 65.
   int e = 0;
   while (c->ev_refs[e] > 0) ++e;
   int st;
@@ -233,7 +284,7 @@ int slots_mark(dita_state_cache* c, hipStream_t s, uint64_t slots) {
     return st;
   if ((st = hip_status(hipEventRecord(c->ev[e], s)))) return st;
   c->ev_stream[e] = static_cast<void*>(s);
-  for (int k = 0; k < c->S; ++k) {
+  for (int k = 0; k < c->S + c->C; ++k) {
     if (!((slots >> k) & 1)) continue;
     if (c->slot_ev[k] >= 0) --c->ev_refs[c->slot_ev[k]];
     c->slot_ev[k] = int16_t(e);
@@ -243,41 +294,78 @@ int slots_mark(dita_state_cache* c, hipStream_t s, uint64_t slots) {
 }
 
 uint64_t slot_bit(int k) { return k >= 0 ? uint64_t(1) << k : 0; }
+// Ordering bit of compact slot j (after the full slots).
+uint64_t cslot_bit(const dita_state_cache* c, int j) { return j >= 0 ? uint64_t(1) << (c->S + j) : 0; }
+// Ordering bit of the slot holding leader p's device state (either format).
+uint64_t state_bit(const dita_state_cache* c, int p) {
+  return c->cphys[p] >= 0 ? cslot_bit(c, c->cphys[p]) : slot_bit(c->phys[p]);
+}
 
-// Compose partitions first..last (validated by the caller: all valid, no
-// group straddling the range) into one group state in slot `first`.
-int compose_range(dita_state_cache* c, int first, int last, hipStream_t stream, int* launched) {
+// Where composing first..last writes the group state: the full slot of
+// `first` if it has one, else that of the first leader in the range with one
+// (the merge then runs in place, that state being source 0), else a free full
+// slot (marked in *taken; out of place).  Returns the slot, -1 if none is
+// free; *src0 is the leader read as source 0 in place, or -1.
+int compose_output(const dita_state_cache* c, int first, int last, uint64_t* taken, int* src0) {
+  *src0 = -1;
+  if (c->phys[first] >= 0) {
+    *src0 = first;
+    return c->phys[first];
+  }
+  for (int p = first + 1; p <= last; ++p)
+    if (c->group[p] == p && c->phys[p] >= 0) {
+      *src0 = p;
+      return c->phys[p];
+    }
+  return take_free(c, taken);
+}
+
+// Number of group leaders in first..last.
+int leaders_in(const dita_state_cache* c, int first, int last) {
+  int n = 0;
+  for (int p = first; p <= last; ++p) n += c->group[p] == p ? 1 : 0;
+  return n;
+}
+
+// Compose partitions first..last (validated by the caller: all valid, every
+// leader on the device, no group straddling the range, and an output slot from
+// compose_output when two or more leaders take part) into one group state held
+// by `first`.
+int compose_range(dita_state_cache* c, int first, int last, int out_k, int src0, hipStream_t stream,
+                  int* launched) {
   // `first` leads its group: no group straddles the range and first is in it.
-  dita::MergeSrc src;
+  dita::MergeSrc src{};
   int n = 0;
   int64_t oldest = c->stamp[first];
-  uint64_t touched = 0;
+  uint64_t touched = slot_bit(out_k);
+  if (src0 >= 0) add_source(c, src, n, src0);
   for (int p = first; p <= last; ++p)
     if (c->group[p] == p) {
-      src.o[n] = slot_o(c, p);
-      src.lse[n] = slot_lse(c, p);
-      touched |= slot_bit(c->phys[p]);
-      ++n;
+      if (p != src0) add_source(c, src, n, p);
+      touched |= state_bit(c, p);
       if (c->stamp[p] < oldest) oldest = c->stamp[p];
     }
   if (n > 1) {
-    // In place: the output is source 0 (slot `first`); each lane reads its
+    // In place when src0 >= 0: the output is source 0; each lane reads its
     // elements of every source before it writes them.
     const dita_shape& s = c->shape;
     const int64_t rows = int64_t(s.B) * s.H * s.Nq;
     int st = slots_wait(c, stream, touched);
     if (st) return st;
     st = hip_status(
-        dita::launch_merge(s.dtype, s.D, rows, n, src, slot_o(c, first), slot_lse(c, first), stream));
+        dita::launch_merge(s.dtype, s.D, rows, n, src, phys_o(c, out_k), phys_lse(c, out_k), stream));
     if (st) return st;
     // The members' slots go back to the pool below: their next owner waits for this merge.
     if ((st = slots_mark(c, stream, touched))) return st;
+    for (int p = first; p <= last; ++p) release(c, p);
+    c->phys[first] = int16_t(out_k);
+  } else {
+    for (int p = first + 1; p <= last; ++p) release(c, p);
   }
   for (int p = first; p <= last; ++p) {
     c->group[p] = int16_t(first);
     c->valid[p] = 1;
     c->stamp[p] = oldest;
-    if (p != first) release(c, p);
   }
   if (launched) *launched = n > 1 ? 1 : 0;
   return DITA_OK;
@@ -353,7 +441,7 @@ int dita_state_merge(const dita_shape* shape, int P, const void* const* o_list,
   if (!o_list || !lse_list) return DITA_ERR_ARG;
   if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
   const size_t ob = state_o_bytes(*shape), lb = state_lse_bytes(*shape);
-  dita::MergeSrc src;
+  dita::MergeSrc src{};
   for (int p = 0; p < P; ++p) {
     if ((st = check_dev(o_list[p])) || (st = check_dev(lse_list[p]))) return st;
     if (overlaps(o_list[p], ob, o, ob) || overlaps(lse_list[p], lb, lse, lb) ||
@@ -376,14 +464,32 @@ size_t dita_state_cache_bytes(const dita_shape* shape, int P) {
 
 namespace {
 
-int cache_init(dita_state_cache** out, const dita_shape* shape, int P, int S, bool pool,
+// Bytes of one compact slot and the offsets of its parts: int8 codes
+// [rows, D], fp32 scales [rows], fp32 LSE [rows], each 256-byte aligned.
+struct CompactLayout {
+  size_t scale_off, lse_off, stride;
+};
+CompactLayout compact_layout(const dita_shape& s) {
+  const size_t rows = size_t(s.B) * size_t(s.H) * size_t(s.Nq);
+  CompactLayout l;
+  l.scale_off = align256(rows * size_t(s.D));
+  l.lse_off = l.scale_off + align256(rows * 4);
+  l.stride = l.lse_off + align256(rows * 4);
+  return l;
+}
+
+int cache_init(dita_state_cache** out, const dita_shape* shape, int P, int S, int C, bool pool,
                void* dev_buf, size_t bytes) {
   if (!out) return DITA_ERR_ARG;
   int st = check_shape(shape);
   if (st) return st;
   if (P < 1 || P > DITA_MAX_PARTITIONS || S < 1 || S > P) return DITA_ERR_SHAPE;
+  if (C < 0 || C > P || S + C > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if (C > 0 && shape->dtype != DITA_BF16) return DITA_ERR_DTYPE;
   if ((st = check_dev(dev_buf))) return st;
-  const size_t need = dita_state_cache_bytes(shape, S);
+  const size_t full = dita_state_cache_bytes(shape, S);
+  const CompactLayout cl = compact_layout(*shape);
+  const size_t need = full + size_t(C) * cl.stride;
   if (bytes < need) return DITA_ERR_SIZE;
   dita_state_cache* c = new (std::nothrow) dita_state_cache;
   if (!c) return DITA_ERR_ARG;
@@ -396,6 +502,11 @@ int cache_init(dita_state_cache** out, const dita_shape* shape, int P, int S, bo
   c->o_bytes = state_o_bytes(*shape);
   c->lse_offset = align256(c->o_bytes);
   c->slot_stride = c->lse_offset + align256(state_lse_bytes(*shape));
+  c->C = C;
+  c->c_base = full;
+  c->c_scale_off = cl.scale_off;
+  c->c_lse_off = cl.lse_off;
+  c->c_stride = cl.stride;
   for (int p = 0; p < DITA_MAX_PARTITIONS; ++p) {
     c->phys[p] = int16_t(pool || p >= P ? -1 : p);
     reset_slot(c, p);
@@ -418,12 +529,74 @@ extern "C" {
 
 int dita_state_cache_init(dita_state_cache** out, const dita_shape* shape, int P, void* dev_buf,
                           size_t bytes) {
-  return cache_init(out, shape, P, P, false, dev_buf, bytes);
+  return cache_init(out, shape, P, P, 0, false, dev_buf, bytes);
 }
 
 int dita_state_cache_init_pool(dita_state_cache** out, const dita_shape* shape, int P, int S,
                                void* dev_buf, size_t bytes) {
-  return cache_init(out, shape, P, S, true, dev_buf, bytes);
+  return cache_init(out, shape, P, S, 0, true, dev_buf, bytes);
+}
+
+size_t dita_state_cache_bytes_compact(const dita_shape* shape, int S, int C) {
+  if (check_shape(shape) || S < 1 || C < 0 || S + C > DITA_MAX_PARTITIONS) return 0;
+  if (C > 0 && shape->dtype != DITA_BF16) return 0;
+  return dita_state_cache_bytes(shape, S) + size_t(C) * compact_layout(*shape).stride;
+}
+
+int dita_state_cache_init_compact(dita_state_cache** out, const dita_shape* shape, int P, int S,
+                                  int C, void* dev_buf, size_t bytes) {
+  return cache_init(out, shape, P, S, C, true, dev_buf, bytes);
+}
+
+int dita_state_cache_compact(dita_state_cache* cache, int p, void* stream) {
+  int st = check_slot(cache, p);
+  if (st) return st;
+  if (cache->C == 0) return DITA_ERR_STATE;
+  if (!resident(cache, p) || cache->cphys[p] >= 0) return DITA_ERR_STATE;
+  const int j = take_free_compact(cache);
+  if (j < 0) return DITA_ERR_SIZE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int k = cache->phys[p];
+  const uint64_t touched = slot_bit(k) | cslot_bit(cache, j);
+  if ((st = slots_wait(cache, hs, touched))) return st;
+  const dita_shape& s = cache->shape;
+  const int64_t rows = int64_t(s.B) * s.H * s.Nq;
+  if ((st = hip_status(dita::launch_compact_encode(s.D, phys_o(cache, k), phys_lse(cache, k),
+                                                   cslot_codes(cache, j), cslot_scale(cache, j),
+                                                   cslot_lse(cache, j), rows, hs))))
+    return st;
+  // The full slot goes back to the pool: its next owner waits for the encoding.
+  if ((st = slots_mark(cache, hs, touched))) return st;
+  release(cache, p);
+  cache->cphys[p] = int16_t(j);
+  return DITA_OK;
+}
+
+int dita_state_cache_compact_slot(const dita_state_cache* cache, int p, void** codes, float** scale,
+                                  float** lse) {
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  const int j = cache->cphys[p];
+  if (j < 0) return DITA_ERR_STATE;
+  if (codes) *codes = cslot_codes(cache, j);
+  if (scale) *scale = cslot_scale(cache, j);
+  if (lse) *lse = cslot_lse(cache, j);
+  return DITA_OK;
+}
+
+int dita_state_cache_format(const dita_state_cache* cache, int p, int* format) {
+  const int st = check_slot(cache, p);
+  if (st) return st;
+  if (!format) return DITA_ERR_ARG;
+  if (!cache->valid[p] || cache->group[p] != p)
+    *format = DITA_STATE_NONE;
+  else if (cache->on_host[p])
+    *format = DITA_STATE_HOST;
+  else if (cache->cphys[p] >= 0)
+    *format = DITA_STATE_COMPACT;
+  else
+    *format = DITA_STATE_FULL;
+  return DITA_OK;
 }
 
 int dita_state_cache_free(dita_state_cache* cache) {
@@ -471,6 +644,7 @@ int dita_state_cache_store(dita_state_cache* cache, int p, const void* o, const 
   if (st) return st;
   if ((st = slots_mark(cache, hs, slot_bit(k)))) return st;
   cache->phys[p] = int16_t(k);
+  cache->cphys[p] = -1;
   forget_host(cache, p);
   cache->valid[p] = 1;
   cache->stamp[p] = step;
@@ -481,7 +655,7 @@ int dita_state_cache_load(const dita_state_cache* cache, int p, void* o, float* 
   int st = check_slot(cache, p);
   if (st) return st;
   if ((st = check_dev(o)) || (st = check_dev(lse))) return st;
-  if (!cache->valid[p] || cache->group[p] != p) return DITA_ERR_STATE;
+  if (!cache->valid[p] || cache->group[p] != p || cache->cphys[p] >= 0) return DITA_ERR_STATE;
   const size_t lb = state_lse_bytes(cache->shape);
   if (overlaps(o, cache->o_bytes, cache->base, cache->bytes) ||
       overlaps(lse, lb, cache->base, cache->bytes))
@@ -538,8 +712,13 @@ int dita_state_cache_compose(dita_state_cache* cache, int first, int last, void*
     if (cache->group[p] < first || group_last(cache, cache->group[p]) > last) return DITA_ERR_ARG;
   }
   for (int p = first; p <= last; ++p)
-    if (cache->group[p] == p && !resident(cache, p)) return DITA_ERR_STATE;  // fetch it first
-  return compose_range(cache, first, last, static_cast<hipStream_t>(stream), nullptr);
+    if (cache->group[p] == p && !on_device(cache, p)) return DITA_ERR_STATE;  // fetch it first
+  int out_k = -1, src0 = -1;
+  if (leaders_in(cache, first, last) > 1) {
+    uint64_t taken = 0;
+    if ((out_k = compose_output(cache, first, last, &taken, &src0)) < 0) return DITA_ERR_SIZE;
+  }
+  return compose_range(cache, first, last, out_k, src0, static_cast<hipStream_t>(stream), nullptr);
 }
 
 int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse, void* stream,
@@ -569,11 +748,20 @@ int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse,
   }
   for (int i = 0; i < n; ++i)
     for (int p = first[i]; p <= last[i]; ++p)
-      if (cache->group[p] == p && !resident(cache, p)) return DITA_ERR_STATE;  // fetch it first
+      if (cache->group[p] == p && !on_device(cache, p)) return DITA_ERR_STATE;  // fetch it first
+  int out_k[DITA_MAX_PARTITIONS], src0[DITA_MAX_PARTITIONS];
+  uint64_t taken = 0;
+  for (int i = 0; i < n; ++i) {
+    out_k[i] = src0[i] = -1;
+    if (leaders_in(cache, first[i], last[i]) > 1 &&
+        (out_k[i] = compose_output(cache, first[i], last[i], &taken, &src0[i])) < 0)
+      return DITA_ERR_SIZE;
+  }
   int launched = 0;
   for (int i = 0; i < n; ++i) {
     int l = 0;
-    const int st = compose_range(cache, first[i], last[i], static_cast<hipStream_t>(stream), &l);
+    const int st = compose_range(cache, first[i], last[i], out_k[i], src0[i],
+                                 static_cast<hipStream_t>(stream), &l);
     if (st) return st;
     launched += l;
   }
@@ -721,8 +909,10 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
 
   // Pooled slots this step writes (fresh, fetched) or reads (reused leaders).
   uint64_t touched = 0;
-  for (int p = 0; p < P; ++p)
-    if (!reuse[p] || cache->group[p] == p) touched |= slot_bit(phys[p]);
+  for (int p = 0; p < P; ++p) {
+    if (reuse[p] && cache->group[p] != p) continue;
+    touched |= (!reuse[p] || cache->on_host[p]) ? slot_bit(phys[p]) : state_bit(cache, p);
+  }
   if ((st = slots_wait(cache, hs, touched))) return st;
 
   if (info && info->ev_begin && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_begin), hs))))
@@ -746,10 +936,17 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
   }
   if (premerge) {
     // Merge the reused states into (o, lse) while the fresh attention runs.
-    dita::MergeSrc pre;
+    dita::MergeSrc pre{};
+    int n_pre = 0;
     for (int i = 0; i < n_reused_heads; ++i) {
-      pre.o[i] = phys_o(cache, phys[reused_heads[i]]);
-      pre.lse[i] = phys_lse(cache, phys[reused_heads[i]]);
+      const int p = reused_heads[i];
+      if (cache->on_host[p]) {  // fetched into phys[p] above
+        pre.o[n_pre] = phys_o(cache, phys[p]);
+        pre.lse[n_pre] = phys_lse(cache, phys[p]);
+        ++n_pre;
+      } else {
+        add_source(cache, pre, n_pre, p);
+      }
     }
     if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_reused_heads, pre, o, lse, side))))
       return st;
@@ -767,6 +964,7 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
       cache->stamp[p] = step;
       cache->group[p] = int16_t(p);
       cache->phys[p] = phys[p];
+      cache->cphys[p] = -1;
       forget_host(cache, p);
     }
   }
@@ -775,19 +973,21 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     forget_host(cache, fetch[i]);
   }
 
-  dita::MergeSrc src;
+  dita::MergeSrc src{};
   int n_src = 0;
+  double src_bytes = 0.0;  // bytes of the states the final merge reads
+  const double compact_bytes = double(rows) * double(s.D + 8);
   if (use_side && (st = hip_status(hipStreamWaitEvent(hs, cache->ev_join, 0)))) return st;
   if (premerge) {
     src.o[n_src] = o;  // the pre-merged reused states; the merge writes it in place
     src.lse[n_src] = lse;
     ++n_src;
+    src_bytes += double(ob + lb);
   }
   for (int p = 0; p < P; ++p) {
     if (cache->group[p] != p || (premerge && reuse[p])) continue;
-    src.o[n_src] = slot_o(cache, p);
-    src.lse[n_src] = slot_lse(cache, p);
-    ++n_src;
+    src_bytes += cache->cphys[p] >= 0 ? compact_bytes : double(ob + lb);
+    add_source(cache, src, n_src, p);
   }
   if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_src, src, o, lse, hs)))) return st;
   if ((st = slots_mark(cache, hs, touched))) return st;
@@ -798,9 +998,12 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     info->n_reused = P - n_fresh;
     info->fresh_flops = 4.0 * double(s.B) * s.H * double(s.Nq) * fresh_keys * s.D;
     info->merge_sources = n_src;
-    info->merge_bytes = double(n_src + 1) * double(ob + lb);
+    info->merge_bytes = src_bytes + double(ob + lb);
     info->premerge_sources = premerge ? n_reused_heads : 0;
-    info->premerge_bytes = premerge ? double(n_reused_heads + 1) * double(ob + lb) : 0.0;
+    double pre_bytes = double(ob + lb);
+    for (int i = 0; i < n_reused_heads; ++i)
+      pre_bytes += cache->cphys[reused_heads[i]] >= 0 ? compact_bytes : double(ob + lb);
+    info->premerge_bytes = premerge ? pre_bytes : 0.0;
     info->fetched = n_fetch;
     info->reserved_out = 0;
   }
@@ -853,17 +1056,18 @@ int dita_state_cache_fetch(dita_state_cache* cache, int p, void* stream) {
 int dita_state_cache_residency(const dita_state_cache* cache, int* on_device, int* on_host,
                                int* free_slots) {
   if (!cache) return DITA_ERR_ARG;
-  int dev = 0, host = 0;
+  int dev = 0, host = 0, full = 0;
   for (int p = 0; p < cache->P; ++p) {
     if (!cache->valid[p] || cache->group[p] != p) continue;
     if (cache->on_host[p])
       ++host;
     else
       ++dev;
+    if (cache->phys[p] >= 0 && !cache->on_host[p] && cache->cphys[p] < 0) ++full;
   }
   if (on_device) *on_device = dev;
   if (on_host) *on_host = host;
-  if (free_slots) *free_slots = cache->S - dev;
+  if (free_slots) *free_slots = cache->S - full;
   return DITA_OK;
 }
 
@@ -891,9 +1095,9 @@ int dita_state_cache_contrib(const dita_state_cache* cache, const float* lse, do
   const float* lses[DITA_MAX_PARTITIONS];
   uint64_t touched = 0;
   for (int p = 0; p < cache->P; ++p) {
-    if (!resident(cache, p) || group_last(cache, p) != p) return DITA_ERR_STATE;
-    lses[p] = slot_lse(cache, p);
-    touched |= slot_bit(cache->phys[p]);
+    if (!on_device(cache, p) || group_last(cache, p) != p) return DITA_ERR_STATE;
+    lses[p] = state_lse(cache, p);
+    touched |= state_bit(cache, p);
   }
   if ((st = check_shape(&cache->shape))) return st;
   dita_state_cache* mc = const_cast<dita_state_cache*>(cache);

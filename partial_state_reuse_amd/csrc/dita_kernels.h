@@ -37,9 +37,13 @@ hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs
 hipError_t launch_attn_f32(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                            hipStream_t stream);
 
+// Sources of a merge.  scale[p] == nullptr: o[p] is a state's output in the
+// merge dtype; otherwise (bf16 merges only) o[p] holds the int8 codes of a
+// compact state and scale[p] its per-row scales.
 struct MergeSrc {
   const void* o[kMaxParts];
   const float* lse[kMaxParts];
+  const float* scale[kMaxParts];
 };
 
 // P-way LSE merge over `rows` = B*H*Nq rows of D elements.  dtype: 0 fp32, 1 bf16.
@@ -62,6 +66,11 @@ int change_groups(size_t o_bytes);
 hipError_t launch_change(int dtype, const void* o_new, void* o_prev, size_t o_bytes,
                          const float* lse_new, float* lse_prev, size_t lse_bytes, int roll,
                          double* partials, double* out, hipStream_t stream);
+
+// Compact encoding of a bf16 state of `rows` rows of D: int8 codes [rows, D],
+// fp32 scale [rows], and the LSE copied to lse_out.
+hipError_t launch_compact_encode(int D, const void* o, const float* lse, int8_t* codes,
+                                 float* scale, float* lse_out, int64_t rows, hipStream_t stream);
 
 // Copy of one attention state (O bytes and LSE bytes, each a multiple of 4 bytes).
 hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,

@@ -26,6 +26,7 @@ namespace dita {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -81,9 +82,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // o and lse may be source 0 (in-place composition and the pre-merged two-stream
 // step), so they are not declared __restrict__: every load of a lane's chunk
 // (and of the row's LSE) feeds the lane's single store of that chunk.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows, T* o,
-                                                         float* lse) {
+//
+// COMPACT (bf16 only): sources whose bit is set in `compact` are compact
+// states -- src.o[j] holds int8 codes in the same [rows, D] layout and
+// src.scale[j] one fp32 scale per row; their values are code * scale (one
+// fp32 product, as the encoding defines).  The lane reads 8 code bytes and the
+// row's scale instead of its 16-byte chunk.
+template <typename T, int D, bool COMPACT>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows,
+                                                         uint64_t compact, T* o, float* lse) {
   constexpr int VN = Vec<T>::N;
   constexpr int LPR = D / VN;          // lanes per row
   constexpr int RPB = kThreads / LPR;  // rows per block
@@ -96,12 +103,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
   // one memory round trip for P <= kChunk.
   u32x4 raw[kChunk];
   float lp[kChunk];
+  float sc[kChunk];
+  auto load_src = [&](int j, int p) {
+    if (COMPACT && ((compact >> p) & 1)) {
+      const u32x2 w = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(src.o[p]) + off));
+      raw[j][0] = w[0];
+      raw[j][1] = w[1];
+      sc[j] = src.scale[p][row];
+    } else {
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(src.o[p]) + off));
+    }
+    lp[j] = src.lse[p][row];
+  };
 #pragma unroll
   for (int j = 0; j < kChunk; ++j) {
-    if (j < P) {
-      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(src.o[j]) + off));
-      lp[j] = src.lse[j][row];
-    }
+    if (j < P) load_src(j, j);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -121,29 +138,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
   // difference is taken first, so the largest state weighs exactly 1 (a
   // one-state merge returns its input unchanged).
   float L = 0.0f;
-  auto accumulate = [&](u32x4 r, float l) {
-    const float w = __builtin_amdgcn_exp2f((l - M) * kLog2e);
+  auto accumulate = [&](int j, int p) {
+    const float w = __builtin_amdgcn_exp2f((lp[j] - M) * kLog2e);
     L += w;
     float x[VN];
-    Vec<T>::unpack(r, x);
+    if (COMPACT && ((compact >> p) & 1)) {
+#pragma unroll
+      for (int i = 0; i < VN; ++i) {
+        const int32_t code = int32_t(raw[j][i / 4] << (24 - 8 * (i % 4))) >> 24;
+        x[i] = float(code) * sc[j];
+      }
+    } else {
+      Vec<T>::unpack(raw[j], x);
+    }
 #pragma unroll
     for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(w, x[i], acc[i]);
   };
 #pragma unroll
   for (int j = 0; j < kChunk; ++j)
-    if (j < P) accumulate(raw[j], lp[j]);
+    if (j < P) accumulate(j, j);
   for (int p0 = kChunk; p0 < P; p0 += kChunk) {
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
-      if (p0 + j < P) {
-        raw[j] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(static_cast<const T*>(src.o[p0 + j]) + off));
-        lp[j] = src.lse[p0 + j][row];
-      }
+      if (p0 + j < P) load_src(j, p0 + j);
     }
 #pragma unroll
     for (int j = 0; j < kChunk; ++j)
-      if (p0 + j < P) accumulate(raw[j], lp[j]);
+      if (p0 + j < P) accumulate(j, p0 + j);
   }
   const float inv = 1.0f / L;
 #pragma unroll
@@ -158,8 +179,18 @@ hipError_t launch_merge_t(int64_t rows, int P, const MergeSrc& src, void* o, flo
   constexpr int LPR = D / Vec<T>::N;
   constexpr int RPB = kThreads / LPR;
   const int64_t blocks = (rows + RPB - 1) / RPB;
-  merge_kernel<T, D><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(src, P, rows,
-                                                                      static_cast<T*>(o), lse);
+  uint64_t compact = 0;
+  for (int p = 0; p < P; ++p)
+    if (src.scale[p]) compact |= uint64_t(1) << p;
+  if constexpr (sizeof(T) == 2) {
+    if (compact) {
+      merge_kernel<T, D, true><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(
+          src, P, rows, compact, static_cast<T*>(o), lse);
+      return hipGetLastError();
+    }
+  }
+  merge_kernel<T, D, false><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(src, P, rows, 0,
+                                                                             static_cast<T*>(o), lse);
   return hipGetLastError();
 }
 

@@ -506,3 +506,46 @@ def test_binding_rejects_mismatched_tensors_before_calling(monkeypatch):
         with pytest.raises(ValueError):
             fn()
     cache.close()
+
+
+def test_compact_cache_host_only():
+    """Compact-cache geometry and validation: bf16 only, S + C <= 64, the buffer size,
+    and compaction of a slot without a full device state refused before any launch."""
+    bf = dita.Shape(1, 2, 128, dita.DITA_BF16, 100, 0.0)
+    f32 = dita.Shape(1, 2, 128, dita.DITA_F32, 100, 0.0)
+    rows = 2 * 100
+    full = lib.dita_state_cache_bytes(ctypes.byref(bf), 3)
+    a256 = lambda x: (x + 255) // 256 * 256
+    per_compact = a256(rows * 128) + 2 * a256(rows * 4)
+    assert lib.dita_state_cache_bytes_compact(ctypes.byref(bf), 3, 4) == full + 4 * per_compact
+    assert lib.dita_state_cache_bytes_compact(ctypes.byref(bf), 3, 0) == full
+    assert lib.dita_state_cache_bytes_compact(ctypes.byref(f32), 3, 1) == 0
+    assert lib.dita_state_cache_bytes_compact(ctypes.byref(bf), 40, 25) == 0
+    n = lib.dita_state_cache_bytes_compact(ctypes.byref(bf), 3, 4)
+    h = ctypes.c_void_p()
+    assert lib.dita_state_cache_init_compact(ctypes.byref(h), ctypes.byref(f32), 5, 3, 4, FAKE_DEV,
+                                             1 << 30) == dita.DITA_ERR_DTYPE
+    assert lib.dita_state_cache_init_compact(ctypes.byref(h), ctypes.byref(bf), 5, 3, 6, FAKE_DEV,
+                                             1 << 30) == dita.DITA_ERR_SHAPE
+    assert lib.dita_state_cache_init_compact(ctypes.byref(h), ctypes.byref(bf), 5, 3, 4, FAKE_DEV,
+                                             n - 1) == dita.DITA_ERR_SIZE
+    assert lib.dita_state_cache_init_compact(ctypes.byref(h), ctypes.byref(bf), 5, 3, 4, FAKE_DEV,
+                                             n) == 0
+    c = h.value
+    fmt = ctypes.c_int()
+    for p in range(5):
+        assert lib.dita_state_cache_format(c, p, ctypes.byref(fmt)) == 0
+        assert fmt.value == dita.DITA_STATE_NONE
+        assert lib.dita_state_cache_compact(c, p, None) == dita.DITA_ERR_STATE
+        assert lib.dita_state_cache_compact_slot(c, p, None, None, None) == dita.DITA_ERR_STATE
+    assert lib.dita_state_cache_compact(c, 5, None) == dita.DITA_ERR_ARG
+    assert lib.dita_state_cache_format(c, 0, None) == dita.DITA_ERR_ARG
+    on_dev, on_host, free = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.dita_state_cache_residency(c, ctypes.byref(on_dev), ctypes.byref(on_host),
+                                          ctypes.byref(free)) == 0
+    assert (on_dev.value, on_host.value, free.value) == (0, 0, 3)
+    lib.dita_state_cache_free(c)
+    # a cache without compact slots has none to give
+    u = _cache(bf, 2)
+    assert lib.dita_state_cache_compact(u, 0, None) == dita.DITA_ERR_STATE
+    lib.dita_state_cache_free(u)
