@@ -163,12 +163,12 @@ __device__ inline void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int D>
+template <int D, int QB_ = 2>
 struct Tile {
   static constexpr int D_ = D;
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int QB = 2;                       // 32-query blocks per wave
+  static constexpr int QB = QB_;                     // 32-query blocks per wave
   static constexpr int BM = kWaves * 32 * QB;        // queries per workgroup
   static constexpr int BN = 4096 / D;                // keys per tile: 32 (D=128), 64 (D=64)
   static constexpr int ROW_BYTES = D * 2;            // one K or V row in HBM
@@ -278,22 +278,16 @@ __device__ inline void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
-    const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int QT, float scale_log2) {
-  using T = Tile<D>;
-  constexpr int QB = T::QB;
+// One query tile: QB * 256 query rows from row0 of head bh against job jid's
+// partition (QB = 2: 512-row tiles; QB = 1: 256-row tiles for the tail rows).
+template <int D, int QB>
+__device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__ q,
+                                          const AttnJobs& jobs, int jid, int64_t bh, int64_t row0,
+                                          int Nq, float scale_log2) {
+  using T = Tile<D, QB>;
   constexpr int NB = T::BN / 32;
   constexpr int NKK = D / 16;
   constexpr int ND = D / 32;
-
-  __shared__ __attribute__((aligned(1024))) char smem[T::NSTAGE * T::STAGE];
-
-  const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(blockIdx.x, int64_t(gridDim.x))));
-  const int qt = __builtin_amdgcn_readfirstlane(lin % QT);
-  const int rest = __builtin_amdgcn_readfirstlane(lin / QT);
-  const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
-  const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
 
   const AttnJob& job = jobs.job[jid];
   const int tid = threadIdx.x;
@@ -316,14 +310,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   bf16x8 qf[QB][NKK];
   // Q of this query tile through a buffer resource whose records end at row Nq:
   // rows past it read as zero, so their (discarded) MFMAs multiply zeros.
-  const int64_t tile_row0 = int64_t(qt) * T::BM;
+  const int64_t tile_row0 = row0;
   const int64_t rows_left = int64_t(Nq) - tile_row0;
   const __amdgpu_buffer_rsrc_t rq =
       tile_rsrc(reinterpret_cast<const char*>(qp + tile_row0 * D), 0, 0,
                 uint32_t((rows_left < T::BM ? rows_left : T::BM) * D * 2));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = qt * T::BM + (wave * QB + qb) * 32 + m32;
+    qrow[qb] = int(row0) + (wave * QB + qb) * 32 + m32;
     const int lrow = (wave * QB + qb) * 32 + m32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -582,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     if ((t + 1) * T::BN > nk) mask_tail(t, sc);
     auto loads_between = [&](int qb) {
       __builtin_amdgcn_sched_barrier(0);
-      if (qb == (wl & 1))
+      if (qb == (QB == 1 ? 0 : (wl & 1)))
         load_share_item<T, 1>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, off_k,
                               off_v);
       __builtin_amdgcn_sched_barrier(0);
@@ -629,14 +623,117 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 }
 
+// Query tiles of one (head, block): `big` 512-row tiles from row 0, then
+// `small` 256-row tiles.
+struct TileSplit {
+  int big;
+  int small;
+};
+
+// Time of a 256-row tile relative to a 512-row tile over the same keys
+// (measured on one MI355X, 4725 keys per head, D = 128).
+constexpr double kSmallTileCost = 0.61;
+
+// Estimated finishing time, in 512-row tile times, of nb 512-row tiles
+// dispatched first and ns 256-row tiles after them, on `cus` compute units
+// that each run one workgroup at a time and take the next tile when free.
+double estimated_makespan(int64_t nb, int64_t ns, int cus, double c1) {
+  const int64_t r = nb / cus, rem = nb % cus;
+  const double big_end = double(r + (rem ? 1 : 0));
+  if (ns == 0) return big_end;
+  // cus - rem units are free at time r, rem at r + 1; each then runs small
+  // tiles back to back.  Hand out the small tiles in order of start time.
+  int64_t left = ns, ma = 0, mb = 0;
+  double last_start = 0.0;
+  while (left > 0) {
+    const double ta = double(r) + double(ma) * c1, tb = double(r + 1) + double(mb) * c1;
+    if (cus - rem > 0 && (rem == 0 || ta <= tb)) {
+      left -= cus - rem;
+      last_start = ta;
+      ++ma;
+    } else {
+      left -= rem;
+      last_start = tb;
+      ++mb;
+    }
+  }
+  const double end = last_start + c1;
+  return end > big_end ? end : big_end;
+}
+
+// The rows past the last whole 512-row tile (4725 = 9 * 512 + 117 rows at the
+// 75,600-token shape) go either into one more 512-row tile or into 256-row
+// tiles, whichever the estimate above finishes first for `per` (head, block)
+// pairs on `cus` compute units.  (Measured: moving more rows than these into
+// 256-row tiles makes launches slower, not faster -- a 256-row tile dispatched
+// at the end of a launch costs more than its 0.61 of a 512-row tile.)
+TileSplit choose_tile_split(int64_t Nq, int64_t per, int cus) {
+  const int whole = int(Nq / 512), all_big = int((Nq + 511) / 512);
+  const TileSplit big_only{all_big, 0};
+  if (whole == all_big) return big_only;
+  const TileSplit with_small{whole, int((Nq - int64_t(whole) * 512 + 255) / 256)};
+  const double t_big = estimated_makespan(int64_t(all_big) * per, 0, cus, kSmallTileCost);
+  const double t_small = estimated_makespan(int64_t(whole) * per, int64_t(with_small.small) * per,
+                                            cus, kSmallTileCost);
+  return t_small < t_big - 1e-9 ? with_small : big_only;
+}
+
+// Compute units of the current device (looked up once per device).
+hipError_t compute_units(int* cus) {
+  static int cached[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) {
+    *cus = cached[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  *cus = n;
+  return hipSuccess;
+}
+
+// Grid: n_big 512-row tiles (QT_big per (head, block), rows [0, 512 QT_big)),
+// then 256-row tiles (QT_small per (head, block), the rows after those), so the
+// smaller tiles are dispatched last and fill the final round.  Each class is
+// remapped on its own so that all tiles of one (head, block) land on one XCD.
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int n_big, int QT_big,
+    int QT_small, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char smem[Tile<D>::NSTAGE * Tile<D>::STAGE];
+  const int pid = blockIdx.x;
+  if (pid < n_big) {
+    const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big)));
+    const int qt = __builtin_amdgcn_readfirstlane(lin % QT_big);
+    const int rest = __builtin_amdgcn_readfirstlane(lin / QT_big);
+    const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+    const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+    attn_tile<D, 2>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq, scale_log2);
+  } else {
+    const int lin =
+        __builtin_amdgcn_readfirstlane(int(xcd_remap(pid - n_big, int64_t(gridDim.x) - n_big)));
+    const int qs = __builtin_amdgcn_readfirstlane(lin % QT_small);
+    const int rest = __builtin_amdgcn_readfirstlane(lin / QT_small);
+    const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+    const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+    attn_tile<D, 1>(smem, q, jobs, jid, bh,
+                    int64_t(QT_big) * Tile<D, 2>::BM + int64_t(qs) * Tile<D, 1>::BM, Nq, scale_log2);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
-                    hipStream_t stream) {
-  using T = Tile<D>;
-  const int QT = int((pr.Nq + T::BM - 1) / T::BM);
-  const int64_t n = int64_t(QT) * pr.BH * n_jobs;
-  attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), T::kThreads, 0, stream>>>(
-      static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, QT, pr.scale * kLog2e);
+                    const TileSplit& split, hipStream_t stream) {
+  const int64_t per = int64_t(pr.BH) * n_jobs;
+  const int64_t n_big = int64_t(split.big) * per;
+  const int64_t n = n_big + int64_t(split.small) * per;
+  attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
+      static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(n_big), split.big, split.small,
+      pr.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -644,8 +741,12 @@ hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, 
 
 hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                             hipStream_t stream) {
-  return pr.D == 128 ? launch_d<128>(pr, q, jobs, n_jobs, stream)
-                     : launch_d<64>(pr, q, jobs, n_jobs, stream);
+  int cus = 0;
+  const hipError_t e = compute_units(&cus);
+  if (e != hipSuccess) return e;
+  const TileSplit split = choose_tile_split(pr.Nq, int64_t(pr.BH) * n_jobs, cus);
+  return pr.D == 128 ? launch_d<128>(pr, q, jobs, n_jobs, split, stream)
+                     : launch_d<64>(pr, q, jobs, n_jobs, split, stream);
 }
 
 }  // namespace dita
