@@ -94,6 +94,10 @@ def parse():
                     help="error planner: compose the runs its next mask reuses after each step")
     ap.add_argument("--planner-anchor", type=int, default=0,
                     help="error planner: anchor period (0: only the cold step)")
+    ap.add_argument("--compact", type=int, default=0, choices=(0, 1),
+                    help="trajectory only: after each step (and its composition ahead) encode "
+                         "every full state the next step reuses into a compact slot (int8 codes, "
+                         "per-row scale); reports the bytes held by cached states per step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the library's state-copy kernel over BYTES of O (the "
                          "reference point for HBM byte counters) and exit")
@@ -330,6 +334,58 @@ def hbm_ceiling(dev, gib: int = 2, reps: int = 5):
             "how": f"torch device copy of {gib} GiB (read + write), best of {reps}"}
 
 
+def sustained_clock(run_step, seconds: float = 4.0):
+    """The shader clock while rank-steps of the schedule run back to back: `amd-smi
+    metric -c` (current clock of every XCD) polled from a thread, the first sample
+    dropped; and the bf16 MFMA peak at that clock.  None when amd-smi is absent."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi")
+    if not exe:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run([exe, "metric", "-c", "-g", "0"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except Exception:
+                return
+            clks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out)]
+            if clks:
+                samples.append(sum(clks) / len(clks))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            run_step(i)
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    used = samples[1:] if len(samples) > 1 else samples
+    if not used:
+        return None
+    mhz = float(np.median(used))   # median: a poll can land in a host-side gap between batches
+    peak = PEAK_BF16_TFLOPS * mhz / 2400.0
+    log(f"[bench] sustained shader clock {mhz:.0f} MHz over {len(used)} samples "
+        f"(bf16 MFMA peak at that clock {peak:.0f} TFLOP/s)")
+    return {"mhz_median": mhz, "mhz_mean": sum(used) / len(used), "mhz_min": min(used),
+            "mhz_max": max(used), "samples": len(used),
+            "steps_run": i, "peak_bf16_TFLOPs": peak,
+            "how": "amd-smi metric -c (mean of the XCDs' current clocks) polled while the "
+                   "schedule's rank-steps ran back to back; median of the polls; peak = "
+                   "2.5 PFLOP/s x clock / 2.4 GHz"}
+
+
 def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 10):
     """One dita_attn_partial call on one 75,600-token block (the rank's queries against
     one partition, all heads), as a caller would make it alone: HIP events on the
@@ -406,7 +462,21 @@ def offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan, reps: int = 3):
     return res
 
 
-def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None):
+def state_bytes_held(dita, cache, wl):
+    """Bytes of the states a cache holds on the device (full: O and LSE; compact:
+    codes, row scales and LSE), and what the same states would take in full."""
+    rows = wl.B * wl.H * wl.Nq
+    full_b, compact_b = rows * (2 * wl.D + 4), rows * (wl.D + 8)
+    held = as_full = 0
+    for p in range(wl.P):
+        f = cache.format(p)
+        if f in (dita.DITA_STATE_FULL, dita.DITA_STATE_COMPACT):
+            held += compact_b if f == dita.DITA_STATE_COMPACT else full_b
+            as_full += full_b
+    return held, as_full
+
+
+def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None, compact=False):
     """The schedule once from a cold cache beside an all-fresh reference (same library,
     same K/V, every partition recomputed): per-step error of the reused output, fresh
     blocks, step latency, and the contribution profile by partition distance."""
@@ -414,7 +484,11 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None
     from workloads import Inputs
     inp = Inputs(wl, seed=seed)
     q = torch.from_numpy(inp.q).to(tdt).to(dev)
-    cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
+    if compact:
+        cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev, slots=wl.P,
+                                compact_slots=wl.P - 1)
+    else:
+        cache = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
     ref = dita.StateCache(wl.B, wl.H, wl.Nq, wl.D, tdt, wl.P, device=dev)
     plan = dita.Plan(**wl.plan_fields())
     shape = (wl.B, wl.H, wl.Nq, wl.D)
@@ -461,6 +535,14 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None
                 cache.compose_runs(planner.mask(s + 1, cache=cache)[0], stream=stream)
         elif compose_ahead and s + 1 < wl.steps:
             cache.compose_runs(dita.dita_plan_mask(plan, s + 1, cache), stream=stream)
+        if compact and s + 1 < wl.steps:
+            nxt = dita.dita_plan_mask(plan, s + 1, cache)
+            for p in range(wl.P):
+                if nxt[p] == 1 and cache.format(p) == dita.DITA_STATE_FULL:
+                    cache.compact(p, stream=stream)
+            held, as_full = state_bytes_held(dita, cache, wl)
+            out.setdefault("state_bytes_held", []).append(held)
+            out.setdefault("state_bytes_if_full", []).append(as_full)
         dita.dita_attn_step(ref, q, ks, vs, all_fresh, s, o=o_ref, lse=lse_ref, stream=stream)
         torch.cuda.synchronize()
         d = o.float() - o_ref.float()
@@ -490,6 +572,11 @@ def trajectory(dita, wl, seed, dev, tdt, stream, compose_ahead=False, eplan=None
         for p in range(wl.P)]
     out["reference"] = ("all-fresh step through the same library on the same K/V "
                         "(every partition recomputed = full attention)")
+    if compact:
+        held, full = sum(out["state_bytes_held"]), sum(out["state_bytes_if_full"])
+        out["compact"] = {"state_bytes_saved_fraction": 1.0 - held / full if full else 0.0,
+                          "note": "bytes held by cached states after each step's compaction, "
+                                  "summed over the steps, against the same states held in full"}
     return out
 
 
@@ -653,6 +740,12 @@ def main():
                      "partly serves, so this is not an HBM figure (isolated.merge is)"),
         },
     }
+    if wl.dtype == "bf16":
+        clk = sustained_clock(lambda i: run(args.warmup + K + i))
+        if clk:
+            result["sustained_clock"] = clk
+            result["roofline"]["peak_at_sustained_clock"] = clk["peak_bf16_TFLOPs"]
+            result["roofline"]["frac_at_sustained_clock"] = achieved / clk["peak_bf16_TFLOPs"]
     result["isolated"] = isolated_bandwidth(dita, wl, tdt, dev, stream, q)
     result["hbm_ceiling"] = hbm_ceiling(dev)
     iso_m = result["isolated"]["merge"]
@@ -671,7 +764,8 @@ def main():
                      "anchor_period": args.planner_anchor, "fresh_weight": args.fresh_weight,
                      "compose_ahead": bool(args.planner_compose)}
         result["trajectory"] = trajectory(dita, wl, args.seed, dev, tdt, stream,
-                                          compose_ahead=bool(args.compose_ahead), eplan=eplan)
+                                          compose_ahead=bool(args.compose_ahead), eplan=eplan,
+                                          compact=bool(args.compact))
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         result["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
