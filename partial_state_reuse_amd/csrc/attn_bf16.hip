@@ -132,6 +132,20 @@ __device__ inline u32x4 k_read(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+// base ^ X computed at this point by one opaque instruction (X = 0: base
+// itself): the compiler can neither hoist the result out of the loop (where it
+// would hold a register the loop cannot spare) nor copy the base first.
+template <int X>
+__device__ inline uint32_t xor_here(uint32_t base) {
+  if constexpr (X == 0) {
+    return base;
+  } else {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "n"(X), "v"(base));
+    return r;
+  }
+}
+
 // Wait until at most N LDS operations are outstanding; the fragments are passed
 // through so that their consumers cannot be scheduled above the wait.
 template <int N>
@@ -216,12 +230,16 @@ __device__ inline uint32_t swz_offset(int slot) {
 // compiler cannot prove uniform turns each load into a read-first-lane loop).
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* head, int t, int tile_bytes,
                                                    uint32_t head_bytes) {
-  const uint32_t start = uint32_t(t) * uint32_t(tile_bytes);
-  const uint32_t left = head_bytes > start ? head_bytes - start : 0u;
+  const uint32_t start = __builtin_amdgcn_readfirstlane(uint32_t(t) * uint32_t(tile_bytes));
+  const uint32_t hb = __builtin_amdgcn_readfirstlane(head_bytes);
+  // max(head_bytes - start, 0) on the scalar unit (written out: the compiler's
+  // saturating subtraction is a vector instruction plus a read-back)
+  uint32_t left;
+  asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=s"(left) : "s"(hb), "s"(start) : "scc");
   const uint64_t addr = reinterpret_cast<uint64_t>(head + start);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(addr));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(addr >> 32));
-  const int n = __builtin_amdgcn_readfirstlane(int(left));
+  const int n = int(left);
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0, n,
                                            0x00020000);
 }
@@ -448,10 +466,10 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
       between(qb);
       part[qb] = exp_block(qb, s, pb);
     }
-    bool ok = true;
+    uint64_t bad = 0;  // lanes whose partial sum is too large or not finite
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) ok = ok && (part[qb] <= kFastLimit);
-    const bool all_ok = !__any(!ok);
+    for (int qb = 0; qb < QB; ++qb) bad |= __builtin_amdgcn_ballot_w64(!(part[qb] <= kFastLimit));
+    const bool all_ok = bad == 0;  // wave-uniform
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += all_ok ? part[qb] : 0.0f;
     return all_ok;
@@ -476,16 +494,12 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
       constexpr int i = decltype(ic)::value;
       if constexpr (i < NPV) {
         constexpr int b = i / (2 * ND), h2 = (i / ND) % 2, d = i % ND;
-        uint32_t a = va;
-        asm volatile("" : "+v"(a));  // computed here, not hoisted and kept live
-        a ^= 64 * d;
+        const uint32_t a = xor_here<64 * d>(va);
         fr[i][0] = tr_read<(32 * b + 16 * h2) * T::ROW_BYTES>(a);
         fr[i][1] = tr_read<(32 * b + 16 * h2 + 8) * T::ROW_BYTES>(a);
       } else {
         constexpr int j = i - NPV, b = j / NKK, kk = j % NKK;
-        uint32_t a = ka;
-        asm volatile("" : "+v"(a));
-        kf[j] = k_read<b * 32 * T::ROW_BYTES>(a ^ (32 * kk));
+        kf[j] = k_read<b * 32 * T::ROW_BYTES>(xor_here<32 * kk>(ka));
       }
     };
     static_for<PF>([&](auto c) {
