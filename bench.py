@@ -98,6 +98,9 @@ def parse():
                     help="trajectory only: after each step (and its composition ahead) encode "
                          "every full state the next step reuses into a compact slot (int8 codes, "
                          "per-row scale); reports the bytes held by cached states per step")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the sustained-clock measurement (it polls amd-smi, a separate "
+                         "program; skipped by itself under a profiler)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the library's state-copy kernel over BYTES of O (the "
                          "reference point for HBM byte counters) and exit")
@@ -740,7 +743,9 @@ def main():
                      "partly serves, so this is not an HBM figure (isolated.merge is)"),
         },
     }
-    if wl.dtype == "bf16":
+    under_profiler = any(k.startswith("ROCPROF") for k in os.environ) or \
+        "rocprof" in os.environ.get("LD_PRELOAD", "")
+    if wl.dtype == "bf16" and not args.no_clock and not under_profiler:
         clk = sustained_clock(lambda i: run(args.warmup + K + i))
         if clk:
             result["sustained_clock"] = clk
