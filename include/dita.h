@@ -108,6 +108,52 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
                       int64_t nk, void* o_p, float* lse_p, void* stream);
 
 /*
+ * Work layout of the bf16 attention kernel (dita_attn_partial, and the fresh
+ * blocks of one dita_attn_step, which share one launch).  Each workgroup takes
+ * a 512-query tile of one (batch, head, block) against all of the block's
+ * keys; rows past the last whole 512-row tile go into one more such tile or
+ * into 256-row tiles, whichever finishes sooner.  When the 512-row tiles do
+ * not fill the last round of the device's compute units, the tiles of that
+ * round are instead computed in pieces along the key axis: split_units
+ * workgroups each take an equal share of those tiles' key-tile iterations
+ * (at most two segments, computed one after the other), and the last piece of a
+ * tile to finish combines the pieces by their LSEs.  That is the pages' state
+ * composition applied to key sub-ranges of one partition (State-Centric
+ * Parallel Runtime > State Composition): exact up to rounding, and the
+ * result does not depend on which piece finishes last.
+ *
+ * The pieces live in a device scratch of scratch_bytes (at most about
+ * 2 x 256 x 264 KiB at D = 128) that the library allocates on the first such
+ * launch on a device and keeps until the process ends.  Launches that use it
+ * from different streams are ordered by an event.  A launch under stream
+ * capture uses the scratch as allocated without waiting or recording (the
+ * caller orders the graph's replays against other attention calls on that
+ * device, e.g. by replaying on the stream they use), and runs without the
+ * split if it would need a larger one.  Blocks of unequal key lengths are not
+ * split.
+ */
+typedef struct {
+  int32_t big_tiles;        /* 512-row tiles per (batch, head, block)                     */
+  int32_t small_tiles;      /* 256-row tiles per (batch, head, block), after the 512-row  */
+  int64_t workgroups;       /* grid size                                                  */
+  int32_t split_units;      /* key-split units; 0: no split                               */
+  int32_t split_tiles;      /* 512-row tiles computed in pieces                           */
+  int32_t max_pieces;       /* most pieces of one split tile                              */
+  int32_t compute_units;    /* of the current device                                      */
+  int64_t scratch_bytes;    /* key-split scratch the launch uses                          */
+} dita_attn_layout;
+
+/*
+ * dita_attn_launch_info -- the layout above for n_blocks (1..DITA_MAX_PARTITIONS)
+ * fresh blocks of nk keys each (nk <= 0: blocks of unequal lengths) of a bf16
+ * problem, on the current device.  Host computation and a device-attribute
+ * query; launches nothing.  DITA_ERR_DTYPE for fp32 problems (their kernel has
+ * no tiles of this kind).
+ */
+int dita_attn_launch_info(const dita_shape* shape, int n_blocks, int64_t nk,
+                          dita_attn_layout* out);
+
+/*
  * dita_state_merge -- exact LSE-weighted composition of P attention states.
  * Page section: State-Centric Parallel Runtime > State Composition
  * (associative, commutative composition of states).

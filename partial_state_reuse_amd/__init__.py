@@ -72,6 +72,13 @@ class ErrorPlan(ctypes.Structure):
                 ("fresh_weight", ctypes.c_double)]
 
 
+class AttnLayout(ctypes.Structure):
+    _fields_ = [("big_tiles", ctypes.c_int32), ("small_tiles", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("split_units", ctypes.c_int32),
+                ("split_tiles", ctypes.c_int32), ("max_pieces", ctypes.c_int32),
+                ("compute_units", ctypes.c_int32), ("scratch_bytes", ctypes.c_int64)]
+
+
 class StepOpts(ctypes.Structure):
     _fields_ = [("side_stream", ctypes.c_void_p), ("min_premerge", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
@@ -93,6 +100,7 @@ def _load() -> ctypes.CDLL:
         "dita_last_hip_error": (i32, []),
         "dita_version": (i32, []),
         "dita_attn_partial": (i32, [ctypes.POINTER(Shape), vp, vp, vp, i64, vp, vp, vp]),
+        "dita_attn_launch_info": (i32, [ctypes.POINTER(Shape), i32, i64, ctypes.POINTER(AttnLayout)]),
         "dita_state_merge": (i32, [ctypes.POINTER(Shape), i32, pvp, pvp, vp, vp, vp]),
         "dita_state_cache_bytes": (sz, [ctypes.POINTER(Shape), i32]),
         "dita_state_cache_init": (i32, [pvp, ctypes.POINTER(Shape), i32, vp, sz]),
@@ -259,6 +267,16 @@ def dita_attn_partial(q, k, v, o=None, lse=None, scale: float = 0.0, stream=None
     _check(_lib.dita_attn_partial(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
                                   _ptr(o), _ptr(lse), _stream(q, stream)), "dita_attn_partial")
     return o, lse
+
+
+def dita_attn_launch_info(B: int, H: int, Nq: int, D: int, n_blocks: int = 1, nk: int = 0) -> dict:
+    """Work layout of the bf16 attention kernel on the current device for ``n_blocks``
+    fresh blocks of ``nk`` keys each (``nk`` <= 0: unequal lengths); see AttnLayout."""
+    out = AttnLayout()
+    shape = Shape(B, H, D, DITA_BF16, Nq, 0.0)
+    _check(_lib.dita_attn_launch_info(ctypes.byref(shape), n_blocks, nk, ctypes.byref(out)),
+           "dita_attn_launch_info")
+    return {name: getattr(out, name) for name, _ in AttnLayout._fields_}
 
 
 def dita_state_merge(o_list: Sequence, lse_list: Sequence, o=None, lse=None, scale: float = 0.0,

@@ -419,7 +419,7 @@ const char* dita_status_str(int status) {
 
 int dita_last_hip_error(void) { return g_last_hip_error; }
 
-int dita_version(void) { return 110; }
+int dita_version(void) { return 111; }
 
 int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
                       int64_t nk, void* o_p, float* lse_p, void* stream) {
@@ -431,6 +431,28 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
   dita::AttnJobs jobs;
   jobs.job[0] = dita::AttnJob{k, v, o_p, lse_p, nk};
   return hip_status(launch_attn(*shape, q, jobs, 1, static_cast<hipStream_t>(stream)));
+}
+
+int dita_attn_launch_info(const dita_shape* shape, int n_blocks, int64_t nk,
+                          dita_attn_layout* out) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!out) return DITA_ERR_ARG;
+  if (shape->dtype != DITA_BF16) return DITA_ERR_DTYPE;
+  if (n_blocks < 1 || n_blocks > DITA_MAX_PARTITIONS) return DITA_ERR_SHAPE;
+  if (nk > 0 && !nk_ok(*shape, nk)) return DITA_ERR_SHAPE;
+  const dita::AttnProblem pr = problem(*shape);
+  dita::AttnLayout l{};
+  if ((st = hip_status(dita::attn_bf16_layout(pr, n_blocks, nk, &l)))) return st;
+  out->big_tiles = l.big;
+  out->small_tiles = l.small;
+  out->workgroups = l.workgroups;
+  out->split_units = l.units;
+  out->split_tiles = l.rem;
+  out->max_pieces = l.max_pieces;
+  out->compute_units = l.cus;
+  out->scratch_bytes = l.scratch;
+  return DITA_OK;
 }
 
 int dita_state_merge(const dita_shape* shape, int P, const void* const* o_list,

@@ -70,8 +70,11 @@
 // and 1.11 with a barrier between every two phases.
 
 #include "dita_kernels.h"
+#include "split_plan.h"
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <utility>
 
 namespace dita {
@@ -197,7 +200,53 @@ struct Tile {
   static constexpr int NSTAGE = 5;
   static_assert(K_WLOADS == kWaves && V_WLOADS == kWaves && STAGE % 1024 == 0,
                 "one K and one V wave-load per wave and stage");
+  // Scratch of one piece of a key-split tile, in the accumulator's register
+  // layout (every lane stores and later reloads 16-byte groups of its own
+  // registers): the unnormalised O^T accumulators, then per lane the running
+  // max and partial denominator of each query block.
+  static constexpr int PIECE_O = kWaves * QB * (D / 32) * 4 * 1024;
+  static constexpr int PIECE = PIECE_O + kWaves * 1024;
 };
+
+// Key-split units of a launch (plan.units == 0: none) and their scratch:
+// 2 * units piece slots of Tile<D>::PIECE bytes, and one arrival counter per
+// remainder tile, zero before the launch and left zero after it.  A unit's
+// range holds at most two segments (it is at most a tile long): the end of the
+// tile it starts in and the start of the next one; one workgroup computes both,
+// one after the other.
+struct SplitArgs {
+  SplitPlan plan;
+  char* pieces;
+  int* count;
+};
+constexpr int kMaxPieces = kSplitMaxPieces;
+
+// Per-workgroup state of a split segment, in LDS rather than in scalar
+// registers: nothing of it stays live through the tile's main loop (the
+// epilogue reads it back after the loop's barriers).
+struct SplitShared {
+  SplitPlan plan;
+  char* pieces;
+  int* count;
+  int64_t unit;
+  int64_t r;       // remainder tile of this segment if it is a piece, else -1
+  int arrived;     // arrivals counted before this workgroup's piece
+};
+__device__ inline SplitShared* split_shared() {
+  __shared__ SplitShared sh;
+  return &sh;
+}
+template <typename V>
+__device__ inline V uniform_lds(const V& v) {
+  if constexpr (sizeof(V) == 8) {
+    const int64_t w = __builtin_bit_cast(int64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(w));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(w) >> 32));
+    return __builtin_bit_cast(V, int64_t((uint64_t(hi) << 32) | lo));
+  } else {
+    return __builtin_bit_cast(V, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  }
+}
 
 // LDS layout of a K or V tile: rows of ROW_BYTES, unpadded, with the 16-byte
 // chunks of each row permuted by an XOR of the row index (physical chunk =
@@ -296,12 +345,179 @@ __device__ inline void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+constexpr int kCoherent = 16;  // buffer cache policy: sc1 (agent scope)
+// Bit casts through by-value parameters (a bit cast of a vector-element lvalue
+// reads element 0).
+__device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// The tile's output from its n pieces (2 <= n <= kMaxPieces) in scratch slots
+// slot[0 .. n-1] (key order): weights from the pieces' running maxima, then
+// per 16-byte group of accumulators the weighted sum, normalised, rounded to
+// bf16 and stored; the loads of four groups of all pieces are issued before
+// any is used.
+template <int D>
+__device__ __forceinline__ void split_combine(__amdgpu_buffer_rsrc_t rs, const uint32_t (&slot)[kMaxPieces],
+                                              int n, int wave, int lane, const int (&qrow)[2], int Nq,
+                                              __bf16* o_head, float* lse_head) {
+  using T = Tile<D, 2>;
+  constexpr int ND = D / 32;
+  constexpr int G = 4;  // 16-byte groups per batch of loads
+  const uint32_t lane_off = uint32_t(lane) * 16;
+  const uint32_t stats_off = uint32_t(T::PIECE_O + wave * 1024) + lane_off;
+  float ms[kMaxPieces][2], ls[kMaxPieces][2];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    ms[i][0] = ms[i][1] = -INFINITY;
+    ls[i][0] = ls[i][1] = 0.0f;
+    if (i < n) {
+      const u32x4 st = __builtin_amdgcn_raw_buffer_load_b128(rs, stats_off, slot[i], kCoherent);
+      ms[i][0] = u2f(st[0]);
+      ls[i][0] = u2f(st[1]);
+      ms[i][1] = u2f(st[2]);
+      ls[i][1] = u2f(st[3]);
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = ms[0][qb];
+#pragma unroll
+    for (int i = 1; i < kMaxPieces; ++i) mx = fmaxf(mx, ms[i][qb]);
+    float w[kMaxPieces];
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) w[i] = __builtin_amdgcn_exp2f(ms[i][qb] - mx);
+    float l = w[0] * ls[0][qb];
+#pragma unroll
+    for (int i = 1; i < kMaxPieces; ++i)
+      if (i < n) l = __builtin_fmaf(w[i], ls[i][qb], l);
+    const float l_tot = l + __shfl_xor(l, 32);
+    const float inv = 1.0f / l_tot;
+    const bool valid = qrow[qb] < Nq;
+    __bf16* __restrict__ op = o_head + int64_t(valid ? qrow[qb] : 0) * D;
+    const uint32_t base = uint32_t(((wave * 2 + qb) * ND * 4) * 64 * 16) + lane_off;
+    for (int c0 = 0; c0 < ND * 4; c0 += G) {
+      u32x4 x[G][kMaxPieces];
+#pragma unroll
+      for (int i = 0; i < kMaxPieces; ++i)
+        if (i < n) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            x[g][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + uint32_t((c0 + g) * 1024),
+                                                            slot[i], kCoherent);
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = w[0] * u2f(x[g][0][e]);
+#pragma unroll
+        for (int i = 1; i < kMaxPieces; ++i)
+          if (i < n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w[i], u2f(x[g][i][e]), acc[e]);
+          }
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[e] * inv);
+        const int c = c0 + g, d = c >> 2, j = c & 3;
+        if (valid) *reinterpret_cast<bf16x4*>(op + d * 32 + 8 * j + 4 * (lane >> 5)) = v;
+      }
+    }
+    if (valid && lane < 32) lse_head[qrow[qb]] = (mx + __builtin_log2f(l_tot)) * kLn2;
+  }
+}
+
+// Pieces of a key-split tile (QB = 2).  Every piece stores its unnormalised
+// state; the piece that arrives last at the tile's counter reloads all of them
+// (its own included) and writes the tile's output: the weighted sum over the
+// pieces in key order, one 16-byte group of accumulators at a time.  Every
+// value is read from the scratch, so the result does not depend on which piece
+// finished last.
+//
+// Ordering across XCDs (each has its own L2) without whole-cache fences: the
+// piece is stored and reloaded with agent-scope coherent accesses (the sc1
+// cache policy, the encoding of agent-scope atomic stores and loads); every
+// wave waits for its stores to complete before the workgroup barrier after
+// which one thread increments the tile's counter (an agent-scope atomic); the
+// combining workgroup issues its reloads only after that increment returned.
+// A completed coherent store is visible to every later coherent load, and the
+// counter's increments are totally ordered, so the last piece sees all others.
+// It resets the counter to zero for the next launch.  (Agent-scope release
+// and acquire fences would write back and invalidate the whole L2 of the XCD
+// for every piece, under the other workgroups' K/V tiles: measured 4-9% slower
+// launches than these per-access scopes.)
+template <int D>
+__device__ __forceinline__ void split_piece(const f32x16 (&oacc)[2][D / 32], const float (&m_run)[2],
+                                            const float (&l_run)[2], int64_t r, int wave, int lane,
+                                            const int (&qrow)[2], int Nq, __bf16* o_head,
+                                            float* lse_head) {
+  using T = Tile<D, 2>;
+  constexpr int ND = D / 32;
+  SplitShared* sh = split_shared();
+  SplitPlan p;
+  p.units = uniform_lds(sh->plan.units);
+  p.rem = uniform_lds(sh->plan.rem);
+  p.T = uniform_lds(sh->plan.T);
+  p.G = uniform_lds(sh->plan.G);
+  char* const pieces = uniform_lds(sh->pieces);
+  int* const count = uniform_lds(sh->count);
+  const int64_t unit = uniform_lds(sh->unit);
+  // One buffer resource over all 2U slots (< 2^32 bytes); a slot is the scalar offset.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      pieces, 0, int(uint32_t(2 * p.units) * uint32_t(T::PIECE)), 0x00020000);
+  const uint32_t lane_off = uint32_t(lane) * 16;
+  auto chunk_off = [&](int qb, int c) {
+    return uint32_t((((wave * 2 + qb) * ND * 4 + c) * 64) * 16) + lane_off;
+  };
+  const uint32_t stats_off = uint32_t(T::PIECE_O + wave * 1024) + lane_off;
+  auto slot_base = [&](int64_t u) {
+    return __builtin_amdgcn_readfirstlane(uint32_t(split_slot(p, u, r)) * uint32_t(T::PIECE));
+  };
+
+  const uint32_t own = slot_base(unit);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = f2u(oacc[qb][d][4 * j + e]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, chunk_off(qb, d * 4 + j), own, kCoherent);
+      }
+  {
+    u32x4 v;
+    v[0] = f2u(m_run[0]);
+    v[1] = f2u(l_run[0]);
+    v[2] = f2u(m_run[1]);
+    v[3] = f2u(l_run[1]);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, stats_off, own, kCoherent);
+  }
+  wait_loads();  // vmcnt(0): this wave's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sh->arrived = __hip_atomic_fetch_add(count + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int n = split_pieces(p, r);
+  if (uniform_lds(sh->arrived) != n - 1) return;
+  if (threadIdx.x == 0) __hip_atomic_store(count + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const int64_t first = split_first_unit(p, r);
+  uint32_t slot[kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) slot[i] = slot_base(first + (i < n ? i : 0));
+  split_combine<D>(rs, slot, n, wave, lane, qrow, Nq, o_head, lse_head);
+}
+
 // One query tile: QB * 256 query rows from row0 of head bh against job jid's
-// partition (QB = 2: 512-row tiles; QB = 1: 256-row tiles for the tail rows).
-template <int D, int QB>
+// partition (QB = 2: 512-row tiles; QB = 1: 256-row tiles for the tail rows),
+// over the partition's key tiles [kt0, kt1) (kt1 < 0: to the end).  A 512-row
+// tile whose split state (LDS) names a remainder tile is a piece of it.
+template <int D, int QB, bool SPLIT = false, int SEG = 0>
 __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__ q,
                                           const AttnJobs& jobs, int jid, int64_t bh, int64_t row0,
-                                          int Nq, float scale_log2) {
+                                          int Nq, float scale_log2, int kt0 = 0, int kt1 = -1) {
   using T = Tile<D, QB>;
   constexpr int NB = T::BN / 32;
   constexpr int NKK = D / 16;
@@ -315,14 +531,27 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
   const int wl = wave & 3;
   const int m32 = lane & 31;
   const int hh = lane >> 5;
-  const int nk = int(job.nk);
-  const int ntiles = (nk + T::BN - 1) / T::BN;
+  // Keys of this tile: all of the partition's, or (split launches) its key
+  // tiles [kt0, kt1) (kt1 < 0: to the end).
+  int nk, ntiles;
+  int64_t key_off;
+  if constexpr (SPLIT) {
+    const int nk_all = int(job.nk);
+    const int kt_end = kt1 < 0 ? (nk_all + T::BN - 1) / T::BN : kt1;
+    nk = min(nk_all - kt0 * T::BN, (kt_end - kt0) * T::BN);
+    ntiles = kt_end - kt0;
+    key_off = bh * int64_t(nk_all) * T::ROW_BYTES + int64_t(kt0) * T::TILE_BYTES;
+  } else {
+    nk = int(job.nk);
+    ntiles = (nk + T::BN - 1) / T::BN;
+    key_off = bh * int64_t(uint32_t(nk) * T::ROW_BYTES);
+  }
 
   const uint32_t head_bytes = uint32_t(nk) * T::ROW_BYTES;
   const uint32_t off_k = swz_offset<T, true>(wave * 64 + lane);
   const uint32_t off_v = swz_offset<T, false>(wave * 64 + lane);
-  const char* k_head = reinterpret_cast<const char*>(job.k) + bh * int64_t(head_bytes);
-  const char* v_head = reinterpret_cast<const char*>(job.v) + bh * int64_t(head_bytes);
+  const char* k_head = reinterpret_cast<const char*>(job.k) + key_off;
+  const char* v_head = reinterpret_cast<const char*>(job.v) + key_off;
   const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
   int qrow[QB];
   bf16x8 qf[QB][NKK];
@@ -617,12 +846,32 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
   }
   wait_loads();  // the zero-filling loads past the last stage must land before LDS is released
 
+  // Split launches: lane indices of the epilogue derived anew behind an opaque
+  // copy (values computed from them are not kept live from the first segment
+  // into the second), and pieces of split tiles handled here.
+  int lane_e = lane, hh_e = hh, qrow_e[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qrow_e[qb] = qrow[qb];
+  if constexpr (SPLIT && QB == 2) {
+    int tid_e = int(threadIdx.x);
+    asm volatile("" : "+v"(tid_e));
+    lane_e = tid_e & 63;
+    hh_e = lane_e >> 5;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) qrow_e[qb] = int(row0) + (wave * QB + qb) * 32 + (lane_e & 31);
+    const int64_t piece_r = uniform_lds(split_shared()->r);
+    if (piece_r >= 0) {
+      split_piece<D>(oacc, m_run, l_run, piece_r, wave, lane_e, qrow_e, Nq,
+                     static_cast<__bf16*>(job.o) + bh * Nq * int64_t(D), job.lse + bh * Nq);
+      return;
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    if (qrow[qb] < Nq) {
+    if (qrow_e[qb] < Nq) {
       const float inv = 1.0f / l_tot;
-      __bf16* __restrict__ op = static_cast<__bf16*>(job.o) + (bh * Nq + qrow[qb]) * int64_t(D);
+      __bf16* __restrict__ op = static_cast<__bf16*>(job.o) + (bh * Nq + qrow_e[qb]) * int64_t(D);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -630,9 +879,9 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
           bf16x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = (__bf16)(oacc[qb][d][4 * j + r] * inv);
-          *reinterpret_cast<bf16x4*>(op + d * 32 + 8 * j + 4 * hh) = v;
+          *reinterpret_cast<bf16x4*>(op + d * 32 + 8 * j + 4 * hh_e) = v;
         }
-      if (hh == 0) job.lse[bh * Nq + qrow[qb]] = (m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
+      if (hh_e == 0) job.lse[bh * Nq + qrow_e[qb]] = (m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
     }
   }
 }
@@ -693,11 +942,12 @@ TileSplit choose_tile_split(int64_t Nq, int64_t per, int cus) {
 }
 
 // Compute units of the current device (looked up once per device).
-hipError_t compute_units(int* cus) {
+hipError_t compute_units(int* cus, int* device = nullptr) {
   static int cached[64] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (device) *device = dev;
   if (dev >= 0 && dev < 64 && cached[dev] > 0) {
     *cus = cached[dev];
     return hipSuccess;
@@ -710,57 +960,273 @@ hipError_t compute_units(int* cus) {
   return hipSuccess;
 }
 
-// Grid: n_big 512-row tiles (QT_big per (head, block), rows [0, 512 QT_big)),
-// then 256-row tiles (QT_small per (head, block), the rows after those), so the
-// smaller tiles are dispatched last and fill the final round.  Each class is
-// remapped on its own so that all tiles of one (head, block) land on one XCD.
-template <int D>
+// Grid, in dispatch order: n_big 512-row tiles (QT_big per (head, block) in
+// linear order, remapped so that all tiles of one (head, block) land on one
+// XCD), n_small 256-row tiles (QT_small per (head, block), the rows after the
+// 512-row tiles), then sa.plan.units key-split units, which share the linear
+// 512-row tiles [n_big, n_big + sa.plan.rem).  A launch has 256-row tiles or
+// split units, not both; launches with split units use the SPLIT instantiation
+// (the other carries none of the split's code).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int n_big, int QT_big,
-    int QT_small, float scale_log2) {
+    int n_small, int QT_small, SplitArgs sa, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char smem[Tile<D>::NSTAGE * Tile<D>::STAGE];
   const int pid = blockIdx.x;
-  if (pid < n_big) {
-    const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big)));
-    const int qt = __builtin_amdgcn_readfirstlane(lin % QT_big);
-    const int rest = __builtin_amdgcn_readfirstlane(lin / QT_big);
-    const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
-    const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
-    attn_tile<D, 2>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq, scale_log2);
+  if constexpr (!SPLIT) {
+    if (pid < n_big) {
+      const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big)));
+      const int qt = __builtin_amdgcn_readfirstlane(lin % QT_big);
+      const int rest = __builtin_amdgcn_readfirstlane(lin / QT_big);
+      const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+      const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+      attn_tile<D, 2>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq, scale_log2);
+    } else {
+      const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid - n_big, n_small)));
+      const int qs = __builtin_amdgcn_readfirstlane(lin % QT_small);
+      const int rest = __builtin_amdgcn_readfirstlane(lin / QT_small);
+      const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+      const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+      attn_tile<D, 1>(smem, q, jobs, jid, bh,
+                      int64_t(QT_big) * Tile<D, 2>::BM + int64_t(qs) * Tile<D, 1>::BM, Nq,
+                      scale_log2);
+    }
+    return;
   } else {
-    const int lin =
-        __builtin_amdgcn_readfirstlane(int(xcd_remap(pid - n_big, int64_t(gridDim.x) - n_big)));
-    const int qs = __builtin_amdgcn_readfirstlane(lin % QT_small);
-    const int rest = __builtin_amdgcn_readfirstlane(lin / QT_small);
-    const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
-    const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
-    attn_tile<D, 1>(smem, q, jobs, jid, bh,
-                    int64_t(QT_big) * Tile<D, 2>::BM + int64_t(qs) * Tile<D, 1>::BM, Nq, scale_log2);
+    SplitShared* sh = split_shared();
+    int64_t lin, r = -1, second_end = 0;
+    int kt0 = 0, kt1 = -1;
+    if (pid < n_big) {
+      lin = xcd_remap(pid, n_big);
+    } else {
+      // Split unit u: its range [x, hi) is at most a tile long; the first
+      // segment runs to the end of the tile it starts in (or to hi), the second
+      // from the next tile boundary to hi.
+      const int64_t u = pid - n_big;
+      const int T = sa.plan.T;
+      const int64_t x = split_lo(sa.plan, u), hi = split_lo(sa.plan, u + 1);
+      const int64_t edge = (x / T + 1) * T;
+      r = x / T;
+      kt0 = int(x - r * T);
+      kt1 = int((hi < edge ? hi : edge) - r * T);
+      if (hi > edge) second_end = hi - edge;
+      lin = n_big + r;
+      if (kt0 == 0 && kt1 == T) r = -1;  // a unit range that is exactly one tile
+      if (threadIdx.x == 0) {
+        sh->plan = sa.plan;
+        sh->pieces = sa.pieces;
+        sh->count = sa.count;
+        sh->unit = u;
+      }
+    }
+    if (threadIdx.x == 0) sh->r = r;
+    __syncthreads();  // the split state is written before any wave reads it
+    {
+      const int qt = __builtin_amdgcn_readfirstlane(int(lin % QT_big));
+      const int rest = __builtin_amdgcn_readfirstlane(int(lin / QT_big));
+      const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+      const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+      attn_tile<D, 2, true>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq, scale_log2,
+                            kt0, kt1);
+    }
+    if (second_end == 0) return;
+    // The unit's second segment: key tiles [0, second_end) of the next tile.
+    // Its parameters are recomputed from the block index, not kept live through
+    // the first segment's main loop.
+    __syncthreads();  // the first segment's LDS reads are done
+    {
+      const int64_t u2 = int64_t(blockIdx.x) - n_big;
+      const int T = sa.plan.T;
+      const int64_t x = split_lo(sa.plan, u2), hi = split_lo(sa.plan, u2 + 1);
+      const int64_t r2 = x / T + 1;
+      const int kt1b = int(hi - r2 * T);
+      const int64_t lin2 = n_big + r2;
+      if (threadIdx.x == 0) sh->r = kt1b == T ? -1 : r2;
+      __syncthreads();
+      const int qt = __builtin_amdgcn_readfirstlane(int(lin2 % QT_big));
+      const int rest = __builtin_amdgcn_readfirstlane(int(lin2 / QT_big));
+      const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
+      const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
+      attn_tile<D, 2, true, 1>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq,
+                               scale_log2, 0, kt1b);
+    }
   }
 }
 
+// Launch layout: 512-row and 256-row tiles per (head, block), and the key
+// split of the remainder (sa.plan.units == 0: none; the scratch pointers are
+// filled in at launch).
+struct LaunchPlan {
+  TileSplit split;
+  int64_t n_big;
+  int64_t n_small;
+  SplitArgs sa;
+};
+
+// Extra cost of one split segment (restarting the K/V pipeline, storing the
+// piece, reloading the pieces it combines), in key-tile iterations.
+constexpr int kSegmentCost = 4;
+// Measured on one MI355X (4725 keys per block, 40 heads, D = 128): a split
+// unit's key-tile iteration takes 1.1-1.2x a whole tile's when the block's K
+// and V sit in the memory-side cache and ~1.85x when they come from HBM (a
+// whole tile shares every K/V tile with the other query tiles of its (head,
+// block) running beside it on the XCD; a unit streams its own key range), and
+// the whole-tile rounds before the units end over a spread of ~0.07 tile
+// times per round (a unit starts when its compute unit frees up).  The
+// planner takes the HBM figure: a single call on 4725 x 4725 x 40 heads (one
+// round and a 0.56 remainder) measured 11% slower split, three blocks (four
+// rounds and a 0.69 remainder) 2% slower; launches with fewer tiles than
+// compute units are split (the units' parallelism outweighs the lost sharing).
+constexpr double kSplitIterCost = 1.85;
+constexpr double kRoundSpread = 0.07;
+// Arrival counters of a launch (one per remainder tile) in the scratch.
+constexpr size_t kCounterBytes = kSplitMaxCounters * sizeof(int);
+
+LaunchPlan plan_launch(int64_t Nq, int64_t per, int cus, int T) {
+  LaunchPlan lp{};
+  lp.split = choose_tile_split(Nq, per, cus);
+  lp.n_big = int64_t(lp.split.big) * per;
+  lp.n_small = int64_t(lp.split.small) * per;
+  if (T < 2) return lp;  // keys of unequal length (T = 0) or a single key tile: no split
+  const int all_big = int((Nq + 511) / 512);
+  const int64_t n = int64_t(all_big) * per;
+  const int64_t rem = n % cus;
+  if (rem == 0) return lp;
+  const double t_tiles = estimated_makespan(lp.n_big, lp.n_small, cus, kSmallTileCost);
+  // Early reject by the split's best case (the most units, hence the shortest
+  // ranges) before the planner checks every tile's pieces.
+  const int64_t most_units = std::min<int64_t>(std::min(cus, kSplitMaxUnits),
+                                               rem * std::min(kSplitMaxUnitsPerTile, T));
+  if (most_units <= rem) return lp;
+  const double best = double(n / cus) * (1.0 + kRoundSpread) +
+                      kSplitIterCost * double((rem * T + most_units - 1) / most_units +
+                                              2 * kSegmentCost) / double(T);
+  if (best >= 0.97 * t_tiles) return lp;
+  double t_units = 0.0;
+  const SplitPlan sk = plan_key_split(n, cus, T, kSegmentCost, &t_units);
+  const double rounds = double(n / cus);
+  const double t_split = rounds * (1.0 + kRoundSpread) + kSplitIterCost * (t_units - rounds);
+  if (sk.units > 0 && t_split < 0.97 * t_tiles) {
+    lp.split = TileSplit{all_big, 0};
+    lp.n_big = n - sk.rem;
+    lp.n_small = 0;
+    lp.sa.plan = sk;
+  }
+  return lp;
+}
+
+// Scratch of the key split, one per device, kept until the process ends:
+// arrival counters (zeroed when allocated; every launch leaves them zero) and
+// piece slots.  Launches that use it are ordered by an event when they come
+// from different streams.  Under stream capture the scratch is used as it is
+// (a captured launch does not wait or record; replays are ordered by the
+// caller, e.g. on the stream the other calls use); one that would need a
+// larger scratch runs without the split.
+struct SplitScratch {
+  std::mutex mu;
+  char* base = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  hipStream_t last = nullptr;
+  bool used = false;
+};
+SplitScratch g_scratch[64];
+
 template <int D>
-hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
-                    const TileSplit& split, hipStream_t stream) {
-  const int64_t per = int64_t(pr.BH) * n_jobs;
-  const int64_t n_big = int64_t(split.big) * per;
-  const int64_t n = n_big + int64_t(split.small) * per;
-  attn_fwd_bf16_kernel<D><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
-      static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(n_big), split.big, split.small,
-      pr.scale * kLog2e);
+hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs,
+                    const LaunchPlan& lp, hipStream_t stream) {
+  const int64_t n_split = lp.sa.plan.units;
+  const int64_t n = lp.n_big + lp.n_small + n_split;
+  if (n_split == 0)
+    attn_fwd_bf16_kernel<D, false><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e);
+  else
+    attn_fwd_bf16_kernel<D, true><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
+                        LaunchPlan& lp, int cus, int dev, hipStream_t stream) {
+  if (lp.sa.plan.units == 0) return launch_d<D>(pr, q, jobs, lp, stream);
+  SplitScratch& w = g_scratch[dev];
+  std::lock_guard<std::mutex> lock(w.mu);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  const size_t need = kCounterBytes + size_t(2) * lp.sa.plan.units * Tile<D>::PIECE;
+  if (w.bytes < need) {
+    if (capturing)  // no allocation under capture: the layout without the split
+      return launch_d<D>(pr, q, jobs, plan_launch(pr.Nq, int64_t(pr.BH) * n_jobs, cus, 0), stream);
+    if (w.used && (e = hipEventSynchronize(w.done)) != hipSuccess) return e;
+    if (w.base && (e = hipFree(w.base)) != hipSuccess) return e;
+    w.base = nullptr;
+    w.bytes = 0;
+    w.used = false;
+    if ((e = hipMalloc(&w.base, need)) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(w.base, 0, kCounterBytes, stream)) != hipSuccess) return e;
+    w.bytes = need;
+  }
+  if (!capturing) {
+    if (!w.done && (e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming)) != hipSuccess)
+      return e;
+    if (w.used && w.last != stream && (e = hipStreamWaitEvent(stream, w.done, 0)) != hipSuccess)
+      return e;
+  }
+  lp.sa.count = reinterpret_cast<int*>(w.base);
+  lp.sa.pieces = w.base + kCounterBytes;
+  if ((e = launch_d<D>(pr, q, jobs, lp, stream)) != hipSuccess) return e;
+  if (!capturing) {
+    if ((e = hipEventRecord(w.done, stream)) != hipSuccess) return e;
+    w.last = stream;
+    w.used = true;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
-                            hipStream_t stream) {
+hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnLayout* out) {
   int cus = 0;
   const hipError_t e = compute_units(&cus);
   if (e != hipSuccess) return e;
-  const TileSplit split = choose_tile_split(pr.Nq, int64_t(pr.BH) * n_jobs, cus);
-  return pr.D == 128 ? launch_d<128>(pr, q, jobs, n_jobs, split, stream)
-                     : launch_d<64>(pr, q, jobs, n_jobs, split, stream);
+  const int BN = 4096 / pr.D;
+  const int T = nk > 0 ? int((nk + BN - 1) / BN) : 0;
+  const LaunchPlan lp = plan_launch(pr.Nq, int64_t(pr.BH) * n_jobs, cus, T);
+  const int units = lp.sa.plan.units;
+  out->big = lp.split.big;
+  out->small = lp.split.small;
+  out->units = units;
+  out->rem = units > 0 ? lp.sa.plan.rem : 0;
+  int most = 0;
+  for (int64_t r = 0; r < out->rem; ++r) most = std::max(most, split_pieces(lp.sa.plan, r));
+  out->max_pieces = most;
+  out->workgroups = lp.n_big + lp.n_small + units;
+  out->cus = cus;
+  const int piece = pr.D == 128 ? Tile<128>::PIECE : Tile<64>::PIECE;
+  out->scratch = units > 0 ? int64_t(kCounterBytes) + int64_t(2) * units * piece : 0;
+  return hipSuccess;
+}
+
+hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
+                            hipStream_t stream) {
+  int cus = 0, dev = 0;
+  const hipError_t e = compute_units(&cus, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  // The key split needs one key length for every block of the launch.
+  int T = 0;
+  const int BN = 4096 / pr.D;
+  bool same = n_jobs > 0;
+  for (int j = 1; j < n_jobs; ++j) same &= jobs.job[j].nk == jobs.job[0].nk;
+  if (same) T = int((jobs.job[0].nk + BN - 1) / BN);
+  LaunchPlan lp = plan_launch(pr.Nq, int64_t(pr.BH) * n_jobs, cus, T);
+  return pr.D == 128 ? launch_split<128>(pr, q, jobs, n_jobs, lp, cus, dev, stream)
+                     : launch_split<64>(pr, q, jobs, n_jobs, lp, cus, dev, stream);
 }
 
 }  // namespace dita

@@ -33,6 +33,16 @@ struct AttnProblem {
 // bf16 Q/K/V/O, MFMA with fp32 accumulation.  Launches grid.z = n_jobs.
 hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                             hipStream_t stream);
+// Work layout launch_attn_bf16 uses on the current device for n_jobs blocks of
+// nk keys each (nk <= 0: blocks of unequal lengths).
+struct AttnLayout {
+  int big, small;      // 512-row and 256-row tiles per (head, block)
+  int64_t workgroups;
+  int units, rem, max_pieces;
+  int cus;
+  int64_t scratch;     // bytes of the key-split scratch
+};
+hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnLayout* out);
 // fp32 throughout.
 hipError_t launch_attn_f32(const AttnProblem& pr, const void* q, const AttnJobs& jobs, int n_jobs,
                            hipStream_t stream);
