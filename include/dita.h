@@ -122,15 +122,15 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
  * Parallel Runtime > State Composition): exact up to rounding, and the
  * result does not depend on which piece finishes last.
  *
- * The pieces live in a device scratch of scratch_bytes (at most about
- * 2 x 256 x 264 KiB at D = 128) that the library allocates on the first such
- * launch on a device and keeps until the process ends.  Launches that use it
- * from different streams are ordered by an event.  A launch under stream
- * capture uses the scratch as allocated without waiting or recording (the
- * caller orders the graph's replays against other attention calls on that
- * device, e.g. by replaying on the stream they use), and runs without the
- * split if it would need a larger one.  Blocks of unequal key lengths are not
- * split.
+ * The pieces live in a device scratch that the library allocates on the first
+ * such launch on a device (scratch_allocated bytes: 2 x 256 x 264 KiB + 16
+ * KiB, about 138 MB, the most any launch uses) and keeps, at the same address,
+ * until the process ends.  Launches that use it from different streams are
+ * ordered by an event.  A launch under stream capture uses it without
+ * waiting or recording (the caller orders the graph's replays against other
+ * attention calls on that device, e.g. by replaying on the stream they use);
+ * one captured before the scratch exists runs without the split.  Blocks of
+ * unequal key lengths are not split.
  */
 typedef struct {
   int32_t big_tiles;        /* 512-row tiles per (batch, head, block)                     */
@@ -141,6 +141,7 @@ typedef struct {
   int32_t max_pieces;       /* most pieces of one split tile                              */
   int32_t compute_units;    /* of the current device                                      */
   int64_t scratch_bytes;    /* key-split scratch the launch uses                          */
+  int64_t scratch_allocated;/* device scratch the library holds for splits (per device)   */
 } dita_attn_layout;
 
 /*

@@ -452,6 +452,7 @@ int dita_attn_launch_info(const dita_shape* shape, int n_blocks, int64_t nk,
   out->max_pieces = l.max_pieces;
   out->compute_units = l.cus;
   out->scratch_bytes = l.scratch;
+  out->scratch_allocated = l.scratch_allocated;
   return DITA_OK;
 }
 

@@ -1115,13 +1115,16 @@ LaunchPlan plan_launch(int64_t Nq, int64_t per, int cus, int T) {
   return lp;
 }
 
-// Scratch of the key split, one per device, kept until the process ends:
-// arrival counters (zeroed when allocated; every launch leaves them zero) and
-// piece slots.  Launches that use it are ordered by an event when they come
-// from different streams.  Under stream capture the scratch is used as it is
-// (a captured launch does not wait or record; replays are ordered by the
-// caller, e.g. on the stream the other calls use); one that would need a
-// larger scratch runs without the split.
+// Scratch of the key split, one per device: arrival counters (zeroed when
+// allocated; every launch leaves them zero) and piece slots for the most
+// units any launch uses, at D = 128 (the larger pieces).  Allocated once, on
+// the first split launch on the device, and never moved or freed, so a launch
+// captured in a graph keeps a valid address for every replay.  Launches that
+// use it are ordered by an event when they come from different streams.  A
+// launch under stream capture uses it as it is, without waiting or recording
+// (the caller orders replays, e.g. on the stream the other calls use); one
+// captured before the scratch exists runs without the split.
+constexpr size_t kScratchBytes = kCounterBytes + size_t(2) * kSplitMaxUnits * Tile<128>::PIECE;
 struct SplitScratch {
   std::mutex mu;
   char* base = nullptr;
@@ -1158,18 +1161,18 @@ hipError_t launch_split(const AttnProblem& pr, const void* q, const AttnJobs& jo
   hipError_t e = hipStreamIsCapturing(stream, &cap);
   if (e != hipSuccess) return e;
   const bool capturing = cap != hipStreamCaptureStatusNone;
-  const size_t need = kCounterBytes + size_t(2) * lp.sa.plan.units * Tile<D>::PIECE;
-  if (w.bytes < need) {
+  static_assert(sizeof(int) * kSplitMaxCounters == kCounterBytes, "counter region");
+  if (lp.sa.plan.units > kSplitMaxUnits || lp.sa.plan.rem > kSplitMaxCounters)
+    return hipErrorInvalidValue;  // the planner keeps to both
+  if (!w.base) {
     if (capturing)  // no allocation under capture: the layout without the split
       return launch_d<D>(pr, q, jobs, plan_launch(pr.Nq, int64_t(pr.BH) * n_jobs, cus, 0), stream);
-    if (w.used && (e = hipEventSynchronize(w.done)) != hipSuccess) return e;
-    if (w.base && (e = hipFree(w.base)) != hipSuccess) return e;
-    w.base = nullptr;
-    w.bytes = 0;
-    w.used = false;
-    if ((e = hipMalloc(&w.base, need)) != hipSuccess) return e;
+    if ((e = hipMalloc(&w.base, kScratchBytes)) != hipSuccess) {
+      w.base = nullptr;
+      return e;
+    }
     if ((e = hipMemsetAsync(w.base, 0, kCounterBytes, stream)) != hipSuccess) return e;
-    w.bytes = need;
+    w.bytes = kScratchBytes;
   }
   if (!capturing) {
     if (!w.done && (e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming)) != hipSuccess)
@@ -1209,6 +1212,7 @@ hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnL
   out->cus = cus;
   const int piece = pr.D == 128 ? Tile<128>::PIECE : Tile<64>::PIECE;
   out->scratch = units > 0 ? int64_t(kCounterBytes) + int64_t(2) * units * piece : 0;
+  out->scratch_allocated = units > 0 ? int64_t(kScratchBytes) : 0;
   return hipSuccess;
 }
 

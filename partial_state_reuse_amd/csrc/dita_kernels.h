@@ -40,7 +40,8 @@ struct AttnLayout {
   int64_t workgroups;
   int units, rem, max_pieces;
   int cus;
-  int64_t scratch;     // bytes of the key-split scratch
+  int64_t scratch;     // bytes of the key-split scratch this launch uses
+  int64_t scratch_allocated;  // bytes the library holds for it per device
 };
 hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnLayout* out);
 // fp32 throughout.

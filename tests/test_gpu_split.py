@@ -42,7 +42,7 @@ def _check_layout(lay, H, nq, n_blocks):
     assert lay["split_units"] > lay["split_tiles"], lay
     assert lay["workgroups"] == n - lay["split_tiles"] + lay["split_units"], lay
     assert 2 <= lay["max_pieces"] <= 5, lay
-    assert lay["scratch_bytes"] > 0, lay
+    assert 0 < lay["scratch_bytes"] <= lay["scratch_allocated"], lay
 
 
 # (H, nq, nk, D): several pieces per tile; ragged query rows and a last key
@@ -164,8 +164,9 @@ def test_split_on_two_streams(dev):
 
 
 def test_split_in_captured_graph(dev):
-    """A split launch captured in a HIP graph (after an eager call sized the
-    scratch) replays bit for bit, with other eager work between the replays."""
+    """A split launch captured in a HIP graph (after an eager call made the
+    scratch) replays bit for bit, with other eager work between the replays,
+    larger split launches among it."""
     import torch
     import partial_state_reuse_amd as dita
     H, nq, nk, D = 2, 517, 2049, 128
@@ -180,10 +181,16 @@ def test_split_in_captured_graph(dev):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         dita.dita_attn_partial(tq, tk, tv, o=o, lse=lse)
+    # between replays: other work, and eager split launches with more units
+    # than the captured one (the scratch must keep its address for the graph)
+    big = _inputs(rng, 6, 1000, 3000, D)
+    bq, bk, bv = (to_dev(x, "bf16", dev) for x in big)
+    assert _layout(6, 1000, D, 1, 3000)["split_units"] > _layout(H, nq, D, 1, nk)["split_units"]
     for r in range(4):
         o.zero_()
         lse.fill_(-1.0)
         junk = torch.randn(1 << 20, device=dev).sum()
+        dita.dita_attn_partial(bq, bk, bv)
         g.replay()
         torch.cuda.synchronize()
         assert bool((o == o_ref).all()) and bool((lse == l_ref).all()), f"replay {r}"
