@@ -415,6 +415,42 @@ def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 10):
             "note": "one block, all heads: Q [1,40,4725,128] against one 4725-key partition"}
 
 
+def short_query_partial(dita, wl, tdt, dev, stream, q, kv0, rows: int = 512, reps: int = 10):
+    """One dita_attn_partial call with few query tiles: the first `rows` of the
+    rank's queries against the whole sequence's keys (all partitions' K/V
+    concatenated), all heads.  One 512-row tile per head leaves most compute
+    units idle, so the library splits the tiles along the keys (reported with
+    its launch layout).  HIP events on the launch stream, median of `reps`."""
+    import torch
+    ks, vs = kv0
+    rows = min(rows, wl.Nq)
+    qs = q[:, :, :rows].contiguous()
+    k = torch.cat([x for x in ks], dim=2)
+    v = torch.cat([x for x in vs], dim=2)
+    nk = k.shape[2]
+    o = torch.empty_like(qs)
+    lse = torch.empty((wl.B, wl.H, rows), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream)
+    times = []
+    for _ in range(reps):
+        b, e = dita.Event(), dita.Event()
+        b.record(stream)
+        dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream)
+        e.record(stream)
+        times.append(b.elapsed_ms(e))
+    ms = float(np.median(times))
+    flops = 4.0 * wl.B * wl.H * rows * nk * wl.D
+    tf = flops / (ms / 1e3) / 1e12
+    layout = dita.dita_attn_launch_info(wl.B, wl.H, rows, wl.D, 1, nk)
+    log(f"[bench] short-query dita_attn_partial ({rows} x {nk}): {ms:.3f} ms = {tf:.0f} TFLOP/s, "
+        f"{layout['split_units']} split units")
+    del k, v
+    return {"ms_median": ms, "flops": flops, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS,
+            "layout": layout,
+            "note": f"Q [1,{wl.H},{rows},{wl.D}] against all {nk} keys: one query tile per head"}
+
+
 def offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan, reps: int = 3):
     """A non-anchor step whose composed far group was moved to pinned host memory:
     step time with the group resident, fetched on the step's stream, and fetched
@@ -757,6 +793,7 @@ def main():
     iso_m["frac_measured_ceiling"] = iso_m["GBps"] / result["hbm_ceiling"]["GBps"]
     if wl.dtype == "bf16":
         result["lone_attn_partial"] = lone_partial(dita, wl, tdt, dev, stream, q, kv[0])
+        result["short_query_partial"] = short_query_partial(dita, wl, tdt, dev, stream, q, kv[0])
     if wl.steps > 1 and n_res > 1:
         result["offload"] = offload_overlap(dita, wl, tdt, dev, stream, q, kv, plan)
     if args.trajectory:

@@ -67,6 +67,23 @@ def test_split_partial_matches_oracle(dev, H, nq, nk, D):
     say(f"  O err {eo:.2e}  LSE err {el:.2e}")
 
 
+def test_split_with_batches_matches_oracle(dev):
+    """B = 2: tiles decode through B * H (heads of both batch entries)."""
+    import partial_state_reuse_amd as dita
+    B, H, nq, nk, D = 2, 3, 600, 3001, 128
+    lay = dita.dita_attn_launch_info(B, H, nq, D, 1, nk)
+    say(f"[split] batches layout={lay}")
+    _check_layout(lay, B * H, nq, 1)
+    rng = np.random.default_rng(29)
+    q = round_bf16(rng.standard_normal((B, H, nq, D)).astype(np.float32) * np.float32(1.5))
+    k = round_bf16(rng.standard_normal((B, H, nk, D)).astype(np.float32) * np.float32(1.5))
+    v = round_bf16(rng.standard_normal((B, H, nk, D)).astype(np.float32) * np.float32(0.5))
+    o, lse = dita.dita_attn_partial(to_dev(q, "bf16", dev), to_dev(k, "bf16", dev),
+                                    to_dev(v, "bf16", dev))
+    o_ref, lse_ref = partial_state(q, k, v)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "split, B = 2")
+
+
 def test_split_peaked_scores_matches_oracle(dev):
     """Keys sorted by score, so the running max moves in every piece and the
     pieces' maxima differ widely: the combination's weights span many octaves."""
