@@ -111,8 +111,10 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
  * Work layout of the bf16 attention kernel (dita_attn_partial, and the fresh
  * blocks of one dita_attn_step, which share one launch).  Each workgroup takes
  * a 512-query tile of one (batch, head, block) against all of the block's
- * keys; rows past the last whole 512-row tile go into one more such tile or
- * into 256-row tiles, whichever finishes sooner.  When the 512-row tiles do
+ * keys; rows past the last whole 512-row tile go into one more such tile, into
+ * 256-row tiles, or (at most 128 of them, blocks of one key length) into
+ * 256-row workgroups that each take the tail rows of two (batch, head, block)
+ * pairs, one per half, whichever finishes sooner.  When the 512-row tiles do
  * not fill the last round of the device's compute units, the tiles of that
  * round are instead computed in pieces along the key axis: split_units
  * workgroups each take an equal share of those tiles' key-tile iterations
@@ -135,6 +137,7 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
 typedef struct {
   int32_t big_tiles;        /* 512-row tiles per (batch, head, block)                     */
   int32_t small_tiles;      /* 256-row tiles per (batch, head, block), after the 512-row  */
+  int32_t dual_tails;       /* 1: each 256-row workgroup takes the tails of two pairs     */
   int64_t workgroups;       /* grid size                                                  */
   int32_t split_units;      /* key-split units; 0: no split                               */
   int32_t split_tiles;      /* 512-row tiles computed in pieces                           */

@@ -74,7 +74,7 @@ class ErrorPlan(ctypes.Structure):
 
 class AttnLayout(ctypes.Structure):
     _fields_ = [("big_tiles", ctypes.c_int32), ("small_tiles", ctypes.c_int32),
-                ("workgroups", ctypes.c_int64), ("split_units", ctypes.c_int32),
+                ("dual_tails", ctypes.c_int32), ("workgroups", ctypes.c_int64), ("split_units", ctypes.c_int32),
                 ("split_tiles", ctypes.c_int32), ("max_pieces", ctypes.c_int32),
                 ("compute_units", ctypes.c_int32), ("scratch_bytes", ctypes.c_int64),
                 ("scratch_allocated", ctypes.c_int64)]

@@ -446,6 +446,7 @@ int dita_attn_launch_info(const dita_shape* shape, int n_blocks, int64_t nk,
   if ((st = hip_status(dita::attn_bf16_layout(pr, n_blocks, nk, &l)))) return st;
   out->big_tiles = l.big;
   out->small_tiles = l.small;
+  out->dual_tails = l.dual;
   out->workgroups = l.workgroups;
   out->split_units = l.units;
   out->split_tiles = l.rem;

@@ -316,24 +316,19 @@ __device__ inline void load_share_item(char* smem, int s, int ntiles, const char
                                              16, off_v, 0, 0, 0);
   }
 }
-template <typename T>
-__device__ inline void load_share(char* smem, int s, int ntiles, const char* k_head,
-                                  const char* v_head, uint32_t head_bytes, int wave,
-                                  uint32_t off_k, uint32_t off_v) {
-  load_share_item<T, 0>(smem, s, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
-  load_share_item<T, 1>(smem, s, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
-}
-
-// vmcnt waits.  Every wave issues two loads per stage; the wait leaves exactly
-// STAGES later stages plus EXTRA single loads in flight.
+// vmcnt waits.  Every wave issues the same loads for every stage (a K and a V
+// load, or two of each for DUAL tiles); the wait leaves exactly STAGES later
+// stages plus the K loads of EXTRA stages in flight.
 template <int N>
 __device__ inline void wait_vm() {
   static_assert(N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N), expcnt and lgkmcnt not waited for
 }
-template <int STAGES, int EXTRA>
+template <int STAGES, int EXTRA, bool DUAL = false>
 __device__ inline void wait_stages_in_flight() {
-  wait_vm<2 * STAGES + EXTRA>();
+  // DUAL tiles: each wave issues two K and two V loads per stage (EXTRA counts
+  // the K loads of one stage).
+  wait_vm<(DUAL ? 4 : 2) * STAGES + (DUAL ? 2 : 1) * EXTRA>();
 }
 __device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -514,21 +509,37 @@ __device__ __forceinline__ void split_piece(const f32x16 (&oacc)[2][D / 32], con
 // partition (QB = 2: 512-row tiles; QB = 1: 256-row tiles for the tail rows),
 // over the partition's key tiles [kt0, kt1) (kt1 < 0: to the end).  A 512-row
 // tile whose split state (LDS) names a remainder tile is a piece of it.
-template <int D, int QB, bool SPLIT = false, int SEG = 0>
-__device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__ q,
-                                          const AttnJobs& jobs, int jid, int64_t bh, int64_t row0,
-                                          int Nq, float scale_log2, int kt0 = 0, int kt1 = -1) {
+// DUAL (QB = 1): the two wave groups take the tails of two (head, block)
+// pairs, (jid, bh, row0) for waves 0-3 and (jid_b, bh_b, row0_b) for waves
+// 4-7, 128 rows each, each group with its own LDS ring of K/V stages that its
+// four waves fill (two K and two V chunks each per stage).  Both pairs must
+// have the same number of keys (the groups share the per-tile barriers).
+template <int D, int QB, bool SPLIT = false, int SEG = 0, bool DUAL = false>
+__device__ __forceinline__ void attn_tile(char* smem_base, const __bf16* __restrict__ q,
+                                          const AttnJobs& jobs, int jid_a, int64_t bh_a,
+                                          int64_t row0_a, int Nq, float scale_log2, int kt0 = 0,
+                                          int kt1 = -1, int jid_b = 0, int64_t bh_b = 0,
+                                          int64_t row0_b = 0) {
   using T = Tile<D, QB>;
   constexpr int NB = T::BN / 32;
   constexpr int NKK = D / 16;
   constexpr int ND = D / 32;
+  static_assert(!DUAL || QB == 1, "dual tiles are 256-row tiles");
 
-  const AttnJob& job = jobs.job[jid];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int wl = wave & 3;
+  const bool second = DUAL && grp == 1;  // wave-uniform
+  const int jid = second ? jid_b : jid_a;
+  const int64_t bh = second ? bh_b : bh_a;
+  const int64_t row0 = second ? row0_b : row0_a;
+  char* const smem = DUAL ? smem_base + grp * (T::NSTAGE * T::STAGE) : smem_base;
+  const AttnJob& job = jobs.job[jid];
+  // First query block of this wave in its tile, and the tile's rows.
+  const int qblk0 = DUAL ? wl * QB : wave * QB;
+  constexpr int BMW = DUAL ? 4 * 32 * QB : T::BM;
   const int m32 = lane & 31;
   const int hh = lane >> 5;
   // Keys of this tile: all of the partition's, or (split launches) its key
@@ -548,8 +559,14 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
   }
 
   const uint32_t head_bytes = uint32_t(nk) * T::ROW_BYTES;
-  const uint32_t off_k = swz_offset<T, true>(wave * 64 + lane);
-  const uint32_t off_v = swz_offset<T, false>(wave * 64 + lane);
+  // The 1 KB chunks of a stage's K and V regions this wave fills: chunk `wave`
+  // of each, or (DUAL) chunks wl and wl + 4 of its group's ring.
+  const int ck0 = DUAL ? wl : wave;
+  const int ck1 = wl + 4;
+  const uint32_t off_k = swz_offset<T, true>(ck0 * 64 + lane);
+  const uint32_t off_v = swz_offset<T, false>(ck0 * 64 + lane);
+  const uint32_t off_k1 = DUAL ? swz_offset<T, true>(ck1 * 64 + lane) : 0u;
+  const uint32_t off_v1 = DUAL ? swz_offset<T, false>(ck1 * 64 + lane) : 0u;
   const char* k_head = reinterpret_cast<const char*>(job.k) + key_off;
   const char* v_head = reinterpret_cast<const char*>(job.v) + key_off;
   const __bf16* __restrict__ qp = q + bh * int64_t(Nq) * D;
@@ -561,20 +578,32 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
   const int64_t rows_left = int64_t(Nq) - tile_row0;
   const __amdgpu_buffer_rsrc_t rq =
       tile_rsrc(reinterpret_cast<const char*>(qp + tile_row0 * D), 0, 0,
-                uint32_t((rows_left < T::BM ? rows_left : T::BM) * D * 2));
+                uint32_t((rows_left < 0 ? 0 : rows_left < BMW ? rows_left : BMW) * D * 2));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = int(row0) + (wave * QB + qb) * 32 + m32;
-    const int lrow = (wave * QB + qb) * 32 + m32;
+    qrow[qb] = int(row0) + (qblk0 + qb) * 32 + m32;
+    const int lrow = (qblk0 + qb) * 32 + m32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[qb][kk] = as_bf16x8(__builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                      rq, uint32_t(lrow * D * 2 + (kk * 16 + 8 * hh) * 2), 0, 0)));
   }
+  auto load_k = [&](int st) {
+    load_share_item<T, 0>(smem, st, ntiles, k_head, v_head, head_bytes, ck0, off_k, off_v);
+    if constexpr (DUAL)
+      load_share_item<T, 0>(smem, st, ntiles, k_head, v_head, head_bytes, ck1, off_k1, off_v1);
+  };
+  auto load_v = [&](int st) {
+    load_share_item<T, 1>(smem, st, ntiles, k_head, v_head, head_bytes, ck0, off_k, off_v);
+    if constexpr (DUAL)
+      load_share_item<T, 1>(smem, st, ntiles, k_head, v_head, head_bytes, ck1, off_k1, off_v1);
+  };
 #pragma unroll
-  for (int st0 = 0; st0 < 3; ++st0)
-    load_share<T>(smem, st0, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
+  for (int st0 = 0; st0 < 3; ++st0) {
+    load_k(st0);
+    load_v(st0);
+  }
 
   // Per-lane LDS offsets inside a stage; a step adds an immediate and XORs a
   // constant into bits the lane part leaves clear (the stage base is 1 KB aligned):
@@ -759,9 +788,7 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
       // Item 0 of this wave's share of stage load_stage_idx, at a step that
       // differs per wave of the group (staggered use of the address unit).
       if constexpr ((i - FIRST) % 4 == 1 && (i - FIRST) / 4 < 4) {
-        if (load_stage_idx >= 0 && wl == (i - FIRST) / 4)
-          load_share_item<T, 0>(smem, load_stage_idx, ntiles, k_head, v_head, head_bytes, wave,
-                                off_k, off_v);
+        if (load_stage_idx >= 0 && wl == (i - FIRST) / 4) load_k(load_stage_idx);
       }
       // Keep the written order: each step's MFMAs before the next step's wait.
       __builtin_amdgcn_sched_barrier(0);
@@ -781,28 +808,27 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
   // stage s+1 and the K load of stage s+2 in flight.  Stage t is rewritten by
   // stage t+5, whose first load A issues after the barrier that ends tile t+1,
   // when B's softmax of tile t (whose exact path may re-read K tile t) is done.
-  wait_stages_in_flight<2, 0>();  // stage 0 (stages 1, 2 in flight)
+  wait_stages_in_flight<2, 0, DUAL>();  // stage 0 (stages 1, 2 in flight)
   phase_barrier();
   f32x16 sc[QB][NB];
   bf16x8 pb[QB][NB][2];
   if (ntiles > 0) {  // step 0: S only, exact max
     __builtin_amdgcn_s_setprio(1);
     m_phase(Int<NPV>{}, Int<NPV + NS>{}, smem, sc, pb, 3);
-    if (wl >= 2)
-      load_share_item<T, 0>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
+    if (wl >= 2) load_k(3);
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) {
-      wait_stages_in_flight<1, 1>();
+      wait_stages_in_flight<1, 1, DUAL>();
       phase_barrier();
     }
-    load_share_item<T, 1>(smem, 3, ntiles, k_head, v_head, head_bytes, wave, off_k, off_v);
+    load_v(3);
     if (T::BN > nk) mask_tail(0, sc);
     float mx[QB];
     row_max(sc, mx);
     rescale(mx);
     softmax(sc, pb);
     if (grp == 0) {
-      wait_stages_in_flight<2, 0>();
+      wait_stages_in_flight<2, 0, DUAL>();
       phase_barrier();
     }
   }
@@ -812,7 +838,7 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
     m_phase(Int<0>{}, Int<NPV + NS>{}, st, sc, pb, t + 3);
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) {
-      wait_stages_in_flight<1, 1>();
+      wait_stages_in_flight<1, 1, DUAL>();
       phase_barrier();
     }
 
@@ -820,8 +846,7 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
     auto loads_between = [&](int qb) {
       __builtin_amdgcn_sched_barrier(0);
       if (qb == (QB == 1 ? 0 : (wl & 1)))
-        load_share_item<T, 1>(smem, t + 3, ntiles, k_head, v_head, head_bytes, wave, off_k,
-                              off_v);
+        load_v(t + 3);
       __builtin_amdgcn_sched_barrier(0);
     };
     const bool fast = softmax_fast(sc, pb, loads_between);
@@ -835,7 +860,7 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
       softmax(sc, pb);
     }
     if (grp == 0) {
-      wait_stages_in_flight<2, 0>();
+      wait_stages_in_flight<2, 0, DUAL>();
       phase_barrier();
     }
   }
@@ -858,7 +883,7 @@ __device__ __forceinline__ void attn_tile(char* smem, const __bf16* __restrict__
     lane_e = tid_e & 63;
     hh_e = lane_e >> 5;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) qrow_e[qb] = int(row0) + (wave * QB + qb) * 32 + (lane_e & 31);
+    for (int qb = 0; qb < QB; ++qb) qrow_e[qb] = int(row0) + (qblk0 + qb) * 32 + (lane_e & 31);
     const int64_t piece_r = uniform_lds(split_shared()->r);
     if (piece_r >= 0) {
       split_piece<D>(oacc, m_run, l_run, piece_r, wave, lane_e, qrow_e, Nq,
@@ -896,6 +921,9 @@ struct TileSplit {
 // Time of a 256-row tile relative to a 512-row tile over the same keys
 // (measured on one MI355X, 4725 keys per head, D = 128).
 constexpr double kSmallTileCost = 0.61;
+// Time of a 256-row workgroup holding the tails (<= 128 rows each) of two
+// (head, block) pairs, relative to a 512-row tile.
+constexpr double kDualTileCost = 0.70;
 
 // Estimated finishing time, in 512-row tile times, of nb 512-row tiles and ns
 // 256-row tiles on `cus` compute units that each run one workgroup at a time
@@ -971,13 +999,40 @@ hipError_t compute_units(int* cus, int* device = nullptr) {
 // the last sa.plan.rem 512-row tiles in linear order, [n_big, n_big + rem).
 // Launches without split units use the other instantiation, which carries
 // none of the split's code.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool DUAL = false>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int n_big, int QT_big,
-    int n_small, int QT_small, SplitArgs sa, float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char smem[Tile<D>::NSTAGE * Tile<D>::STAGE];
+    int n_small, int QT_small, SplitArgs sa, float scale_log2, int pairs) {
+  __shared__ __attribute__((aligned(1024)))
+  char smem[(DUAL ? 2 : 1) * Tile<D>::NSTAGE * Tile<D>::STAGE];
   const int pid = blockIdx.x;
-  if constexpr (!SPLIT) {
+  if constexpr (DUAL) {
+    // Per two (head, block) pairs: the first's 512-row tiles, the second's,
+    // then one workgroup for both pairs' tail rows (at most 128 each); an odd
+    // last pair shares its tail workgroup with no rows.
+    const int per_unit = 2 * QT_big + 1;
+    const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big + n_small)));
+    const int pp = __builtin_amdgcn_readfirstlane(lin / per_unit);
+    const int j = __builtin_amdgcn_readfirstlane(lin % per_unit);
+    const bool has_b = 2 * pp + 1 < pairs;
+    if (j < (has_b ? 2 * QT_big : QT_big)) {
+      const int pair = __builtin_amdgcn_readfirstlane(2 * pp + (j >= QT_big ? 1 : 0));
+      const int qt = __builtin_amdgcn_readfirstlane(j >= QT_big ? j - QT_big : j);
+      const int64_t bh = __builtin_amdgcn_readfirstlane(pair % BH);
+      const int jid = __builtin_amdgcn_readfirstlane(pair / BH);
+      attn_tile<D, 2>(smem, q, jobs, jid, bh, int64_t(qt) * Tile<D, 2>::BM, Nq, scale_log2);
+    } else {
+      const int pa = 2 * pp, pb = has_b ? 2 * pp + 1 : 2 * pp;
+      const int64_t bh_a = __builtin_amdgcn_readfirstlane(pa % BH);
+      const int jid_a = __builtin_amdgcn_readfirstlane(pa / BH);
+      const int64_t bh_b = __builtin_amdgcn_readfirstlane(pb % BH);
+      const int jid_b = __builtin_amdgcn_readfirstlane(pb / BH);
+      const int64_t tail0 = int64_t(QT_big) * Tile<D, 2>::BM;
+      attn_tile<D, 1, false, 0, true>(smem, q, jobs, jid_a, bh_a, tail0, Nq, scale_log2, 0, -1,
+                                      jid_b, bh_b, has_b ? tail0 : int64_t(Nq));
+    }
+    return;
+  } else if constexpr (!SPLIT) {
     // The tiles of one (head, block) are consecutive, its 256-row tiles right
     // after its 512-row ones, so they read the block's K/V from the same L2.
     const int per_pair = QT_big + QT_small;
@@ -1061,8 +1116,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
 struct LaunchPlan {
   TileSplit split;
   int64_t n_big;
-  int64_t n_small;
+  int64_t n_small;   // 256-row workgroups (DUAL: one per two pairs)
   SplitArgs sa;
+  bool dual;         // tails of two (head, block) pairs per 256-row workgroup
+  int64_t pairs;     // (head, block) pairs of the launch
 };
 
 // Extra cost of one split segment (restarting the K/V pipeline, storing the
@@ -1086,9 +1143,26 @@ constexpr size_t kCounterBytes = kSplitMaxCounters * sizeof(int);
 
 LaunchPlan plan_launch(int64_t Nq, int64_t per, int cus, int T) {
   LaunchPlan lp{};
+  lp.pairs = per;
   lp.split = choose_tile_split(Nq, per, cus);
   lp.n_big = int64_t(lp.split.big) * per;
   lp.n_small = int64_t(lp.split.small) * per;
+  // Tails of at most 128 rows, two per 256-row workgroup (the pairs must have
+  // one key length), when that finishes earlier than either layout above.
+  const int whole = int(Nq / 512);
+  const int64_t tail = Nq - int64_t(whole) * 512;
+  if (T > 0 && tail > 0 && tail <= 128 && per >= 2) {
+    const int64_t n_dual = (per + 1) / 2;
+    const double t_cur = estimated_makespan(lp.n_big, lp.n_small, cus, kSmallTileCost);
+    const double t_dual = estimated_makespan(int64_t(whole) * per, n_dual, cus, kDualTileCost);
+    if (t_dual < t_cur - 1e-9) {
+      lp.split = TileSplit{whole, 1};
+      lp.n_big = int64_t(whole) * per;
+      lp.n_small = n_dual;
+      lp.dual = true;
+      return lp;  // no key split with dual tails
+    }
+  }
   if (T < 2) return lp;  // keys of unequal length (T = 0) or a single key tile: no split
   const int all_big = int((Nq + 511) / 512);
   const int64_t n = int64_t(all_big) * per;
@@ -1142,14 +1216,19 @@ hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs,
                     const LaunchPlan& lp, hipStream_t stream) {
   const int64_t n_split = lp.sa.plan.units;
   const int64_t n = lp.n_big + lp.n_small + n_split;
-  if (n_split == 0)
+  const int pairs = int(lp.pairs);
+  if (n_split == 0 && !lp.dual)
     attn_fwd_bf16_kernel<D, false><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
         static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
-        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e);
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
+  else if (n_split == 0)
+    attn_fwd_bf16_kernel<D, false, true><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
+        static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
   else
     attn_fwd_bf16_kernel<D, true><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
         static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
-        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e);
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
   return hipGetLastError();
 }
 
@@ -1205,6 +1284,7 @@ hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnL
   const int units = lp.sa.plan.units;
   out->big = lp.split.big;
   out->small = lp.split.small;
+  out->dual = lp.dual ? 1 : 0;
   out->units = units;
   out->rem = units > 0 ? lp.sa.plan.rem : 0;
   int most = 0;

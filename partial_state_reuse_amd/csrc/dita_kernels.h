@@ -37,6 +37,7 @@ hipError_t launch_attn_bf16(const AttnProblem& pr, const void* q, const AttnJobs
 // nk keys each (nk <= 0: blocks of unequal lengths).
 struct AttnLayout {
   int big, small;      // 512-row and 256-row tiles per (head, block)
+  int dual;            // 1: each 256-row workgroup takes the tails of two pairs
   int64_t workgroups;
   int units, rem, max_pieces;
   int cus;

@@ -274,3 +274,41 @@ def test_grouped_launch_with_256_row_tiles(dev, D):
         so, sl = cache.slot(p)
         ro, rl = ref.slots[p]
         assert_state_close(to_host(so), to_host(sl), ro, rl, "bf16", f"fresh state {p}")
+
+
+# (H, nq, P, nk, D): tails of 88 or 52 rows; pairs even (320) and odd (287);
+# D = 64 with four whole 512-row tiles before the tail.
+DUAL_CASES = [(40, 600, 8, 700, 128), (41, 600, 7, 700, 128), (40, 2100, 8, 700, 64)]
+
+
+@pytest.mark.parametrize("H,nq,P,nk,D", DUAL_CASES)
+def test_grouped_launch_with_dual_tail_tiles(dev, H, nq, P, nk, D):
+    """A grouped launch whose tail rows (at most 128 per (head, block)) go two
+    pairs per 256-row workgroup, each wave group with its own K/V ring: the
+    library's layout says so, and every head and row of the step output and of
+    every fresh state matches the oracle (an odd pair count leaves the last
+    workgroup's second half without rows)."""
+    import torch
+    import partial_state_reuse_amd as dita
+    from gpu_util import HeadChunkedOracle
+    lay = dita.dita_attn_launch_info(1, H, nq, D, P, nk)
+    say(f"dual tails H={H} nq={nq} P={P} nk={nk} D={D} layout={lay}")
+    assert lay["dual_tails"] == 1 and lay["small_tiles"] == 1 and lay["split_units"] == 0, lay
+    pairs = H * P
+    assert lay["workgroups"] == lay["big_tiles"] * pairs + (pairs + 1) // 2, lay
+    rng = np.random.default_rng(H * 31 + nq + P + D)
+    q = round_bf16(rng.standard_normal((1, H, nq, D)).astype(np.float32) * 1.5)
+    ks = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 1.5) for _ in range(P)]
+    vs = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 0.35) for _ in range(P)]
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    fresh = np.zeros(P, np.uint8)
+    o, lse, info = dita.dita_attn_step(cache, to_dev(q, "bf16", dev), [to_dev(x, "bf16", dev) for x in ks],
+                                       [to_dev(x, "bf16", dev) for x in vs], fresh, 0)
+    assert info.n_fresh == P
+    ref = HeadChunkedOracle(P, H, chunk=max(1, H // 16))
+    o_ref, lse_ref, _ = ref.step(q, ks, vs, fresh, 0)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "dual tails, output")
+    for p in range(P):
+        so, sl = cache.slot(p)
+        ro, rl = ref.slot(p)
+        assert_state_close(to_host(so), to_host(sl), ro, rl, "bf16", f"dual tails, state {p}")
