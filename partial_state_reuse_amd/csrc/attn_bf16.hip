@@ -810,6 +810,30 @@ __device__ __forceinline__ void attn_tile(char* smem_base, const __bf16* __restr
   // when B's softmax of tile t (whose exact path may re-read K tile t) is done.
   wait_stages_in_flight<2, 0, DUAL>();  // stage 0 (stages 1, 2 in flight)
   phase_barrier();
+  // A wave whose query blocks all lie past Nq (the padding rows of a tail
+  // tile) computes nothing: under the board's power cap its MFMAs and
+  // exponentials would only lower the clock of the waves that do.  It keeps
+  // its share of every stage's loads, in the same order, and takes every
+  // barrier of the schedule below, then leaves (its rows are not stored).
+  // Split launches, whose pieces meet at further barriers, keep every wave.
+  if constexpr (!SPLIT) {
+    if (row0 + int64_t(qblk0) * 32 >= Nq) {  // wave-uniform
+      for (int t = 0; t < ntiles; ++t) {
+        load_k(t + 3);
+        if (grp == 1) {
+          wait_stages_in_flight<1, 1, DUAL>();
+          phase_barrier();
+        }
+        load_v(t + 3);
+        if (grp == 0) {
+          wait_stages_in_flight<2, 0, DUAL>();
+          phase_barrier();
+        }
+      }
+      wait_loads();
+      return;
+    }
+  }
   f32x16 sc[QB][NB];
   bf16x8 pb[QB][NB][2];
   if (ntiles > 0) {  // step 0: S only, exact max
