@@ -333,8 +333,31 @@ def hbm_ceiling(dev, gib: int = 2, reps: int = 5):
     del src, dst
     torch.cuda.empty_cache()
     log(f"[bench] HBM ceiling: torch copy of {gib} GiB at {gbs:.0f} GB/s")
+    # The merge's own mix, 16 reads to 1 write: torch's sum over the leading axis
+    # of a [16, n] bf16 tensor (fp32 accumulation inside, bf16 out).
+    rows, cols = 16, 24_192_000  # 16 slots of one 75,600-token state's O
+    x = torch.ones(rows, cols, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(cols, dtype=torch.bfloat16, device=dev)
+    torch.sum(x, dim=0, out=y)
+    torch.cuda.synchronize()
+    best_r = None
+    for _ in range(reps):
+        b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        torch.sum(x, dim=0, out=y)
+        e.record()
+        e.synchronize()
+        ms = b.elapsed_time(e)
+        best_r = ms if best_r is None else min(best_r, ms)
+    r_gbs = (rows + 1) * cols * 2 / (best_r / 1e3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    log(f"[bench] torch 16-to-1 bf16 sum at {r_gbs:.0f} GB/s")
     return {"GBps": gbs, "frac_vendor_peak": gbs / PEAK_HBM_GBS,
-            "how": f"torch device copy of {gib} GiB (read + write), best of {reps}"}
+            "how": f"torch device copy of {gib} GiB (read + write), best of {reps}",
+            "sum16": {"GBps": r_gbs, "frac_vendor_peak": r_gbs / PEAK_HBM_GBS,
+                      "how": f"torch.sum over dim 0 of a [16, {cols}] bf16 tensor "
+                             f"(16 reads : 1 write, the merge's mix), best of {reps}"}}
 
 
 def sustained_clock(run_step, seconds: float = 4.0):
@@ -791,6 +814,7 @@ def main():
     result["hbm_ceiling"] = hbm_ceiling(dev)
     iso_m = result["isolated"]["merge"]
     iso_m["frac_measured_ceiling"] = iso_m["GBps"] / result["hbm_ceiling"]["GBps"]
+    iso_m["frac_sum16"] = iso_m["GBps"] / result["hbm_ceiling"]["sum16"]["GBps"]
     if wl.dtype == "bf16":
         result["lone_attn_partial"] = lone_partial(dita, wl, tdt, dev, stream, q, kv[0])
         result["short_query_partial"] = short_query_partial(dita, wl, tdt, dev, stream, q, kv[0])
