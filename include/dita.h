@@ -114,7 +114,10 @@ int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, con
  * keys; rows past the last whole 512-row tile go into one more such tile, into
  * 256-row tiles, or (at most 128 of them, blocks of one key length) into
  * 256-row workgroups that each take the tail rows of two (batch, head, block)
- * pairs, one per half, whichever finishes sooner.  When the 512-row tiles do
+ * pairs, one per half, whichever finishes sooner.  In the staged layout all
+ * 512-row tiles run before all 256-row tiles, and some pairs trade one 512-row
+ * tile for two 256-row tiles so that the 512-row tiles fill whole rounds of
+ * the device's compute units (staged_pairs below).  When the 512-row tiles do
  * not fill the last round of the device's compute units, the tiles of that
  * round are instead computed in pieces along the key axis: split_units
  * workgroups each take an equal share of those tiles' key-tile iterations
@@ -145,6 +148,11 @@ typedef struct {
   int32_t compute_units;    /* of the current device                                      */
   int64_t scratch_bytes;    /* key-split scratch the launch uses                          */
   int64_t scratch_allocated;/* device scratch the library holds for splits (per device)   */
+  int32_t staged_pairs;     /* >= 0: staged layout, all 512-row tiles dispatched before   */
+                            /* all 256-row tiles; the first staged_pairs pairs have       */
+                            /* big_tiles and small_tiles, the others big_tiles - 1 and    */
+                            /* small_tiles_b.  -1: per-pair order (or no 256-row tiles)   */
+  int32_t small_tiles_b;    /* staged layout: 256-row tiles of the other pairs            */
 } dita_attn_layout;
 
 /*

@@ -77,7 +77,8 @@ class AttnLayout(ctypes.Structure):
                 ("dual_tails", ctypes.c_int32), ("workgroups", ctypes.c_int64), ("split_units", ctypes.c_int32),
                 ("split_tiles", ctypes.c_int32), ("max_pieces", ctypes.c_int32),
                 ("compute_units", ctypes.c_int32), ("scratch_bytes", ctypes.c_int64),
-                ("scratch_allocated", ctypes.c_int64)]
+                ("scratch_allocated", ctypes.c_int64), ("staged_pairs", ctypes.c_int32),
+                ("small_tiles_b", ctypes.c_int32)]
 
 
 class StepOpts(ctypes.Structure):

@@ -419,7 +419,7 @@ const char* dita_status_str(int status) {
 
 int dita_last_hip_error(void) { return g_last_hip_error; }
 
-int dita_version(void) { return 111; }
+int dita_version(void) { return 112; }
 
 int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
                       int64_t nk, void* o_p, float* lse_p, void* stream) {
@@ -454,6 +454,8 @@ int dita_attn_launch_info(const dita_shape* shape, int n_blocks, int64_t nk,
   out->compute_units = l.cus;
   out->scratch_bytes = l.scratch;
   out->scratch_allocated = l.scratch_allocated;
+  out->staged_pairs = l.stage_a;
+  out->small_tiles_b = l.small_b;
   return DITA_OK;
 }
 

@@ -71,6 +71,7 @@
 
 #include "dita_kernels.h"
 #include "split_plan.h"
+#include "tile_layout.h"
 
 #include <algorithm>
 #include <cmath>
@@ -943,52 +944,26 @@ struct TileSplit {
   int small;
 };
 
-// Time of a 256-row tile relative to a 512-row tile over the same keys
-// (measured on one MI355X, 4725 keys per head, D = 128).
-constexpr double kSmallTileCost = 0.61;
 // Time of a 256-row workgroup holding the tails (<= 128 rows each) of two
 // (head, block) pairs, relative to a 512-row tile (from the measured gain of
 // the 16-block launches at the 75,600-token shape: 1.3% against 2.1% for
 // 0.70; each wave loads twice the K/V of a single tail per key tile).
 constexpr double kDualTileCost = 0.85;
 
-// Estimated finishing time, in 512-row tile times, of nb 512-row tiles and ns
-// 256-row tiles on `cus` compute units that each run one workgroup at a time
-// and take the next tile when free, modelled with the 256-row tiles last.
-// (The kernel dispatches each (head, block)'s 256-row tiles right after its
-// 512-row ones instead, so that they share the block's K/V in L2: measured at
-// the same launch times as dispatching them last, with 1.5 GB less HBM
-// traffic per 16-block launch at the 75,600-token shape.)
-double estimated_makespan(int64_t nb, int64_t ns, int cus, double c1) {
-  const int64_t r = nb / cus, rem = nb % cus;
-  const double big_end = double(r + (rem ? 1 : 0));
-  if (ns == 0) return big_end;
-  // cus - rem units are free at time r, rem at r + 1; each then runs small
-  // tiles back to back.  Hand out the small tiles in order of start time.
-  int64_t left = ns, ma = 0, mb = 0;
-  double last_start = 0.0;
-  while (left > 0) {
-    const double ta = double(r) + double(ma) * c1, tb = double(r + 1) + double(mb) * c1;
-    if (cus - rem > 0 && (rem == 0 || ta <= tb)) {
-      left -= cus - rem;
-      last_start = ta;
-      ++ma;
-    } else {
-      left -= rem;
-      last_start = tb;
-      ++mb;
-    }
-  }
-  const double end = last_start + c1;
-  return end > big_end ? end : big_end;
-}
+// (estimated_makespan models the 256-row tiles dispatched after all 512-row
+// tiles.  The interleaved layout dispatches each (head, block)'s 256-row tiles
+// right after its 512-row ones instead, so that they share the block's K/V in
+// L2: measured at the same launch times as dispatching them last, with 1.5 GB
+// less HBM traffic per 16-block launch at the 75,600-token shape.)
 
 // The rows past the last whole 512-row tile (4725 = 9 * 512 + 117 rows at the
 // 75,600-token shape) go either into one more 512-row tile or into 256-row
 // tiles, whichever the estimate above finishes first for `per` (head, block)
 // pairs on `cus` compute units.  (Measured: moving more rows than these into
-// 256-row tiles makes launches slower, not faster -- a 256-row tile costs more
-// in a mixed launch than its 0.61 of a 512-row tile.)
+// 256-row tiles in this per-pair order makes launches slower, not faster: the
+// 512-row tiles then spread over more rounds than the estimate assumes.  The
+// staged layout moves more rows into 256-row tiles, dispatched after all
+// 512-row tiles.)
 TileSplit choose_tile_split(int64_t Nq, int64_t per, int cus) {
   const int whole = int(Nq / 512), all_big = int((Nq + 511) / 512);
   const TileSplit big_only{all_big, 0};
@@ -1026,10 +1001,15 @@ hipError_t compute_units(int* cus, int* device = nullptr) {
 // the last sa.plan.rem 512-row tiles in linear order, [n_big, n_big + rem).
 // Launches without split units use the other instantiation, which carries
 // none of the split's code.
+// Staged layout (stage_a >= 0, no split units, no dual tails): all n_big
+// 512-row tiles first, then all n_small 256-row tiles, each kind remapped by
+// itself; pairs [0, stage_a) have QT_big 512-row and QT_small 256-row tiles,
+// the others QT_big - 1 and QT_small_b.
 template <int D, bool SPLIT, bool DUAL = false>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, AttnJobs jobs, int Nq, int BH, int n_big, int QT_big,
-    int n_small, int QT_small, SplitArgs sa, float scale_log2, int pairs) {
+    int n_small, int QT_small, SplitArgs sa, float scale_log2, int pairs, int stage_a,
+    int QT_small_b) {
   __shared__ __attribute__((aligned(1024)))
   char smem[(DUAL ? 2 : 1) * Tile<D>::NSTAGE * Tile<D>::STAGE];
   const int pid = blockIdx.x;
@@ -1060,21 +1040,33 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     }
     return;
   } else if constexpr (!SPLIT) {
-    // The tiles of one (head, block) are consecutive, its 256-row tiles right
-    // after its 512-row ones, so they read the block's K/V from the same L2.
-    const int per_pair = QT_big + QT_small;
-    const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big + n_small)));
-    const int j = __builtin_amdgcn_readfirstlane(lin % per_pair);
-    const int rest = __builtin_amdgcn_readfirstlane(lin / per_pair);
-    const int64_t bh = __builtin_amdgcn_readfirstlane(rest % BH);
-    const int jid = __builtin_amdgcn_readfirstlane(rest / BH);
-    if (j < QT_big) {
-      attn_tile<D, 2>(smem, q, jobs, jid, bh, int64_t(j) * Tile<D, 2>::BM, Nq, scale_log2);
+    int pair;
+    int64_t row0;
+    bool big;
+    if (stage_a >= 0) {
+      big = pid < n_big;
+      const int lin = __builtin_amdgcn_readfirstlane(
+          int(big ? xcd_remap(pid, n_big) : xcd_remap(pid - n_big, n_small)));
+      const StagedTile st = staged_tile(lin, big, QT_big, QT_small, QT_small_b, stage_a);
+      pair = __builtin_amdgcn_readfirstlane(int(st.pair));
+      row0 = __builtin_amdgcn_readfirstlane(int(st.row0));
     } else {
-      attn_tile<D, 1>(smem, q, jobs, jid, bh,
-                      int64_t(QT_big) * Tile<D, 2>::BM + int64_t(j - QT_big) * Tile<D, 1>::BM, Nq,
-                      scale_log2);
+      // The tiles of one (head, block) are consecutive, its 256-row tiles right
+      // after its 512-row ones, so they read the block's K/V from the same L2.
+      const int per_pair = QT_big + QT_small;
+      const int lin = __builtin_amdgcn_readfirstlane(int(xcd_remap(pid, n_big + n_small)));
+      const int j = __builtin_amdgcn_readfirstlane(lin % per_pair);
+      pair = __builtin_amdgcn_readfirstlane(lin / per_pair);
+      big = j < QT_big;
+      row0 = big ? int64_t(j) * Tile<D, 2>::BM
+                 : int64_t(QT_big) * Tile<D, 2>::BM + int64_t(j - QT_big) * Tile<D, 1>::BM;
     }
+    const int64_t bh = __builtin_amdgcn_readfirstlane(pair % BH);
+    const int jid = __builtin_amdgcn_readfirstlane(pair / BH);
+    if (big)
+      attn_tile<D, 2>(smem, q, jobs, jid, bh, row0, Nq, scale_log2);
+    else
+      attn_tile<D, 1>(smem, q, jobs, jid, bh, row0, Nq, scale_log2);
     return;
   } else {
     SplitShared* sh = split_shared();
@@ -1147,6 +1139,8 @@ struct LaunchPlan {
   SplitArgs sa;
   bool dual;         // tails of two (head, block) pairs per 256-row workgroup
   int64_t pairs;     // (head, block) pairs of the launch
+  int stage_a = -1;  // staged layout: pairs with split.big 512-row tiles (< 0: none)
+  int small_b = 0;   // staged layout: 256-row tiles of the other pairs
 };
 
 // Extra cost of one split segment (restarting the K/V pipeline, storing the
@@ -1168,21 +1162,53 @@ constexpr double kRoundSpread = 0.07;
 // Arrival counters of a launch (one per remainder tile) in the scratch.
 constexpr size_t kCounterBytes = kSplitMaxCounters * sizeof(int);
 
+// Key split of the last round of n 512-row tiles (T key tiles each), if its
+// estimate finishes 3% before t_tiles; units == 0: none.
+SplitPlan choose_key_split(int64_t n, int cus, int T, double t_tiles) {
+  const SplitPlan none{};
+  const int64_t rem = n % cus;
+  if (T < 2 || rem == 0) return none;  // unequal key lengths (T = 0), one key tile, whole rounds
+  // Early reject by the split's best case (the most units, hence the shortest
+  // ranges) before the planner checks every tile's pieces.
+  const int64_t most_units = std::min<int64_t>(std::min(cus, kSplitMaxUnits),
+                                               rem * std::min(kSplitMaxUnitsPerTile, T));
+  if (most_units <= rem) return none;
+  const double best = double(n / cus) * (1.0 + kRoundSpread) +
+                      kSplitIterCost * double((rem * T + most_units - 1) / most_units +
+                                              2 * kSegmentCost) / double(T);
+  if (best >= 0.97 * t_tiles) return none;
+  double t_units = 0.0;
+  const SplitPlan sk = plan_key_split(n, cus, T, kSegmentCost, &t_units);
+  const double rounds = double(n / cus);
+  const double t_split = rounds * (1.0 + kRoundSpread) + kSplitIterCost * (t_units - rounds);
+  return sk.units > 0 && t_split < 0.97 * t_tiles ? sk : none;
+}
+
+// Layout of a launch of `per` (head, block) pairs of Nq query rows, T key
+// tiles each (T = 0: unequal key lengths), on `cus` compute units: dual tails
+// where they finish first; otherwise the key split where it beats the
+// per-pair layouts (measured: it does on launches of few tiles, where the
+// staged layout's estimate can be lower); otherwise the staged layout where
+// its estimate is lower than the per-pair layouts'.
 LaunchPlan plan_launch(int64_t Nq, int64_t per, int cus, int T) {
   LaunchPlan lp{};
   lp.pairs = per;
   lp.split = choose_tile_split(Nq, per, cus);
   lp.n_big = int64_t(lp.split.big) * per;
   lp.n_small = int64_t(lp.split.small) * per;
+  const double t_tiles = estimated_makespan(lp.n_big, lp.n_small, cus, kSmallTileCost);
+  // All 512-row tiles first, sized to fill whole rounds, then all 256-row ones.
+  double t_staged = 0.0;
+  const StagedLayout sl = plan_staged(Nq, per, cus, kSmallTileCost, &t_staged);
+  const bool staged = sl.stage_a >= 0 && t_staged < t_tiles - 1e-9;
   // Tails of at most 128 rows, two per 256-row workgroup (the pairs must have
-  // one key length), when that finishes earlier than either layout above.
+  // one key length), when that finishes earlier than the layouts above.
   const int whole = int(Nq / 512);
   const int64_t tail = Nq - int64_t(whole) * 512;
   if (T > 0 && tail > 0 && tail <= 128 && per >= 2) {
     const int64_t n_dual = (per + 1) / 2;
-    const double t_cur = estimated_makespan(lp.n_big, lp.n_small, cus, kSmallTileCost);
     const double t_dual = estimated_makespan(int64_t(whole) * per, n_dual, cus, kDualTileCost);
-    if (t_dual < t_cur - 1e-9) {
+    if (t_dual < t_tiles - 1e-9 && (!staged || t_dual < t_staged - 1e-9)) {
       lp.split = TileSplit{whole, 1};
       lp.n_big = int64_t(whole) * per;
       lp.n_small = n_dual;
@@ -1190,30 +1216,20 @@ LaunchPlan plan_launch(int64_t Nq, int64_t per, int cus, int T) {
       return lp;  // no key split with dual tails
     }
   }
-  if (T < 2) return lp;  // keys of unequal length (T = 0) or a single key tile: no split
   const int all_big = int((Nq + 511) / 512);
   const int64_t n = int64_t(all_big) * per;
-  const int64_t rem = n % cus;
-  if (rem == 0) return lp;
-  const double t_tiles = estimated_makespan(lp.n_big, lp.n_small, cus, kSmallTileCost);
-  // Early reject by the split's best case (the most units, hence the shortest
-  // ranges) before the planner checks every tile's pieces.
-  const int64_t most_units = std::min<int64_t>(std::min(cus, kSplitMaxUnits),
-                                               rem * std::min(kSplitMaxUnitsPerTile, T));
-  if (most_units <= rem) return lp;
-  const double best = double(n / cus) * (1.0 + kRoundSpread) +
-                      kSplitIterCost * double((rem * T + most_units - 1) / most_units +
-                                              2 * kSegmentCost) / double(T);
-  if (best >= 0.97 * t_tiles) return lp;
-  double t_units = 0.0;
-  const SplitPlan sk = plan_key_split(n, cus, T, kSegmentCost, &t_units);
-  const double rounds = double(n / cus);
-  const double t_split = rounds * (1.0 + kRoundSpread) + kSplitIterCost * (t_units - rounds);
-  if (sk.units > 0 && t_split < 0.97 * t_tiles) {
+  const SplitPlan sk = choose_key_split(n, cus, T, t_tiles);
+  if (sk.units > 0) {
     lp.split = TileSplit{all_big, 0};
     lp.n_big = n - sk.rem;
     lp.n_small = 0;
     lp.sa.plan = sk;
+  } else if (staged) {
+    lp.split = TileSplit{sl.nb, sl.ns_a};
+    lp.n_big = sl.n_big;
+    lp.n_small = sl.n_small;
+    lp.stage_a = sl.stage_a;
+    lp.small_b = sl.ns_b;
   }
   return lp;
 }
@@ -1247,15 +1263,15 @@ hipError_t launch_d(const AttnProblem& pr, const void* q, const AttnJobs& jobs,
   if (n_split == 0 && !lp.dual)
     attn_fwd_bf16_kernel<D, false><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
         static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
-        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs, lp.stage_a, lp.small_b);
   else if (n_split == 0)
     attn_fwd_bf16_kernel<D, false, true><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
         static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
-        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs, lp.stage_a, lp.small_b);
   else
     attn_fwd_bf16_kernel<D, true><<<dim3(unsigned(n)), Tile<D>::kThreads, 0, stream>>>(
         static_cast<const __bf16*>(q), jobs, int(pr.Nq), pr.BH, int(lp.n_big), lp.split.big,
-        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs);
+        int(lp.n_small), lp.split.small, lp.sa, pr.scale * kLog2e, pairs, lp.stage_a, lp.small_b);
   return hipGetLastError();
 }
 
@@ -1312,6 +1328,8 @@ hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnL
   out->big = lp.split.big;
   out->small = lp.split.small;
   out->dual = lp.dual ? 1 : 0;
+  out->stage_a = lp.stage_a;
+  out->small_b = lp.small_b;
   out->units = units;
   out->rem = units > 0 ? lp.sa.plan.rem : 0;
   int most = 0;

@@ -43,6 +43,8 @@ struct AttnLayout {
   int cus;
   int64_t scratch;     // bytes of the key-split scratch this launch uses
   int64_t scratch_allocated;  // bytes the library holds for it per device
+  int stage_a;         // staged layout: pairs with `big` and `small` tiles (< 0: none)
+  int small_b;         // staged layout: 256-row tiles of the other pairs (big - 1 512-row)
 };
 hipError_t attn_bf16_layout(const AttnProblem& pr, int n_jobs, int64_t nk, AttnLayout* out);
 // fp32 throughout.

@@ -278,6 +278,49 @@ def test_grouped_launch_with_256_row_tiles(dev, D):
 
 # (H, nq, P, nk, D): tails of 88 or 52 rows; pairs even (320) and odd (287);
 # D = 64 with four whole 512-row tiles before the tail.
+# (H, nq, P, nk, D) launches that the planner lays out staged on a 256-CU
+# device: every 512-row tile first, then every 256-row tile, with some pairs
+# holding one 512-row tile fewer and two 256-row tiles more (or, last case,
+# 256-row tiles only).
+STAGED_CASES = [(24, 1100, 6, 300, 128), (41, 1300, 5, 300, 64), (12, 1800, 8, 300, 64),
+                (8, 1000, 1, 700, 128)]
+
+
+@pytest.mark.parametrize("H,nq,P,nk,D", STAGED_CASES)
+def test_grouped_launch_with_staged_tiles(dev, H, nq, P, nk, D):
+    """A grouped launch in the staged layout: the library's layout says so, its
+    tile counts add up to the grid, and every head and row of the step output
+    and of every fresh state matches the oracle."""
+    import torch
+    import partial_state_reuse_amd as dita
+    from gpu_util import HeadChunkedOracle
+    lay = dita.dita_attn_launch_info(1, H, nq, D, P, nk)
+    say(f"staged tiles H={H} nq={nq} P={P} nk={nk} D={D} layout={lay}")
+    if lay["compute_units"] != 256:
+        pytest.skip("layout chosen for a 256-CU device")
+    pairs = H * P
+    a = lay["staged_pairs"]
+    assert 0 <= a <= pairs and lay["split_units"] == 0 and lay["dual_tails"] == 0, lay
+    n_big = a * lay["big_tiles"] + (pairs - a) * (lay["big_tiles"] - 1)
+    n_small = a * lay["small_tiles"] + (pairs - a) * lay["small_tiles_b"]
+    assert n_small > 0 and lay["workgroups"] == n_big + n_small, lay
+    rng = np.random.default_rng(H * 37 + nq + P + D)
+    q = round_bf16(rng.standard_normal((1, H, nq, D)).astype(np.float32) * 1.5)
+    ks = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 1.5) for _ in range(P)]
+    vs = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 0.35) for _ in range(P)]
+    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    fresh = np.zeros(P, np.uint8)
+    o, lse, info = dita.dita_attn_step(cache, to_dev(q, "bf16", dev), [to_dev(x, "bf16", dev) for x in ks],
+                                       [to_dev(x, "bf16", dev) for x in vs], fresh, 0)
+    assert info.n_fresh == P
+    ref = HeadChunkedOracle(P, H, chunk=max(1, H // 16))
+    o_ref, lse_ref, _ = ref.step(q, ks, vs, fresh, 0)
+    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "staged tiles, output")
+    for p in range(P):
+        so, sl = cache.slot(p)
+        ro, rl = ref.slot(p)
+        assert_state_close(to_host(so), to_host(sl), ro, rl, "bf16", f"staged tiles, state {p}")
+
 DUAL_CASES = [(40, 600, 8, 700, 128), (41, 600, 7, 700, 128), (40, 2100, 8, 700, 64)]
 
 
