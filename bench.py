@@ -412,30 +412,43 @@ def sustained_clock(run_step, seconds: float = 4.0):
                    "2.5 PFLOP/s x clock / 2.4 GHz"}
 
 
+def _call_times(dita, stream, call, reps: int):
+    """GPU time of each of `reps` calls made back to back on `stream`: one call is
+    queued ahead of the first event, so the host's launch work for each call
+    overlaps the previous call and no interval includes GPU idle time waiting for
+    the host.  Returns the per-call intervals (ms) between consecutive events."""
+    evs = [dita.Event() for _ in range(reps + 1)]
+    call(-1)
+    evs[0].record(stream)
+    for i in range(reps):
+        call(i)
+        evs[i + 1].record(stream)
+    return [evs[i].elapsed_ms(evs[i + 1]) for i in range(reps)]  # waits for each later event
+
+
 def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 10):
     """One dita_attn_partial call on one 75,600-token block (the rank's queries against
-    one partition, all heads), as a caller would make it alone: HIP events on the
-    launch stream around each call, median over `reps` calls."""
+    one partition, all heads): calls back to back on the launch stream, each on
+    another block's K/V (read from HBM), HIP events between them, median of `reps`."""
     import torch
     ks, vs = kv0
     o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
     lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
     for _ in range(3):
         dita.dita_attn_partial(q, ks[1], vs[1], o=o, lse=lse, stream=stream)
-    times = []
-    for i in range(reps):
-        b, e = dita.Event(), dita.Event()
-        b.record(stream)
-        dita.dita_attn_partial(q, ks[1 + i % (wl.P - 1)], vs[1 + i % (wl.P - 1)], o=o, lse=lse,
-                               stream=stream)
-        e.record(stream)
-        times.append(b.elapsed_ms(e))
+
+    def call(i):
+        j = 1 + (i + 1) % (wl.P - 1)
+        dita.dita_attn_partial(q, ks[j], vs[j], o=o, lse=lse, stream=stream)
+
+    times = _call_times(dita, stream, call, reps)
     ms = float(np.median(times))
     tf = wl.block_flops() / (ms / 1e3) / 1e12
     log(f"[bench] lone dita_attn_partial: {ms:.3f} ms = {tf:.0f} TFLOP/s")
     return {"ms_median": ms, "ms_min": float(np.min(times)), "flops": wl.block_flops(),
             "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS,
-            "note": "one block, all heads: Q [1,40,4725,128] against one 4725-key partition"}
+            "note": "one block, all heads: Q [1,40,4725,128] against one 4725-key partition; "
+                    "calls back to back, each on another block's K/V"}
 
 
 def short_query_partial(dita, wl, tdt, dev, stream, q, kv0, rows: int = 512, reps: int = 10):
@@ -443,7 +456,8 @@ def short_query_partial(dita, wl, tdt, dev, stream, q, kv0, rows: int = 512, rep
     rank's queries against the whole sequence's keys (all partitions' K/V
     concatenated), all heads.  One 512-row tile per head leaves most compute
     units idle, so the library splits the tiles along the keys (reported with
-    its launch layout).  HIP events on the launch stream, median of `reps`."""
+    its launch layout).  Calls back to back, HIP events between them, median of
+    `reps`."""
     import torch
     ks, vs = kv0
     rows = min(rows, wl.Nq)
@@ -455,13 +469,8 @@ def short_query_partial(dita, wl, tdt, dev, stream, q, kv0, rows: int = 512, rep
     lse = torch.empty((wl.B, wl.H, rows), dtype=torch.float32, device=dev)
     for _ in range(3):
         dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream)
-    times = []
-    for _ in range(reps):
-        b, e = dita.Event(), dita.Event()
-        b.record(stream)
-        dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream)
-        e.record(stream)
-        times.append(b.elapsed_ms(e))
+    times = _call_times(dita, stream,
+                        lambda i: dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream), reps)
     ms = float(np.median(times))
     flops = 4.0 * wl.B * wl.H * rows * nk * wl.D
     tf = flops / (ms / 1e3) / 1e12
