@@ -426,15 +426,16 @@ def _call_times(dita, stream, call, reps: int):
     return [evs[i].elapsed_ms(evs[i + 1]) for i in range(reps)]  # waits for each later event
 
 
-def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 10):
+def lone_partial(dita, wl, tdt, dev, stream, q, kv0, reps: int = 20):
     """One dita_attn_partial call on one 75,600-token block (the rank's queries against
-    one partition, all heads): calls back to back on the launch stream, each on
-    another block's K/V (read from HBM), HIP events between them, median of `reps`."""
+    one partition, all heads): after ~12 ms of warm-up calls, calls back to back on
+    the launch stream, each on another block's K/V (read from HBM), HIP events
+    between them, median of `reps`."""
     import torch
     ks, vs = kv0
     o = torch.empty((wl.B, wl.H, wl.Nq, wl.D), dtype=tdt, device=dev)
     lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
-    for _ in range(3):
+    for _ in range(30):  # ~12 ms of calls: the clock settles as under the step's load
         dita.dita_attn_partial(q, ks[1], vs[1], o=o, lse=lse, stream=stream)
 
     def call(i):
@@ -467,7 +468,7 @@ def short_query_partial(dita, wl, tdt, dev, stream, q, kv0, rows: int = 512, rep
     nk = k.shape[2]
     o = torch.empty_like(qs)
     lse = torch.empty((wl.B, wl.H, rows), dtype=torch.float32, device=dev)
-    for _ in range(3):
+    for _ in range(15):  # ~12 ms of calls, as for the lone call
         dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream)
     times = _call_times(dita, stream,
                         lambda i: dita.dita_attn_partial(qs, k, v, o=o, lse=lse, stream=stream), reps)
