@@ -703,13 +703,12 @@ def main():
         si = step_index % n_sched
         mask = dita.dita_plan_mask(plan, si, cache)
         ks, vs = kv[si % n_res]
+        # The planner is deterministic: the step composes what the next step will
+        # reuse (every partition is valid after a step, hence no cache for the mask).
+        nxt = dita.dita_plan_mask(plan, (step_index + 1) % n_sched) if args.compose_ahead else None
         _, _, info = dita.dita_attn_step(cache, q, ks, vs, mask, step_index, o=o, lse=lse,
                                          stream=stream, events=events and events[:3],
-                                         side_stream=side)
-        if args.compose_ahead:
-            # the planner is deterministic: compose what the next step will reuse
-            nxt = dita.dita_plan_mask(plan, (step_index + 1) % n_sched, cache)
-            cache.compose_runs(nxt, stream=stream)
+                                         side_stream=side, compose_next=nxt)
         if events:
             assert dita.lib().dita_event_record(events[3], stream.cuda_stream) == 0
         return info

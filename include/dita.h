@@ -462,7 +462,8 @@ typedef struct {
   int32_t n_fresh;          /* [out] partitions computed fresh                          */
   int32_t n_reused;         /* [out] partitions reused                                  */
   double fresh_flops;       /* [out] 4*B*H*Nq*sum(nk of fresh)*D                        */
-  double merge_bytes;       /* [out] (merge_sources + 1) * bytes of one state           */
+  double merge_bytes;       /* [out] bytes the final merge moves: its sources and its   */
+                            /*       output(s) (a group composed in the same pass too)  */
   void* ev_begin;           /* [in] hipEvent_t or NULL                                  */
   void* ev_attn_end;        /* [in] hipEvent_t or NULL                                  */
   void* ev_end;             /* [in] hipEvent_t or NULL                                  */
@@ -470,7 +471,8 @@ typedef struct {
   int32_t premerge_sources; /* [out] reused states pre-merged on the side stream, or 0  */
   double premerge_bytes;    /* [out] (premerge_sources + 1) * bytes of one state, or 0  */
   int32_t fetched;          /* [out] reused states copied back from host memory         */
-  int32_t reserved_out;     /* [out] 0                                                  */
+  int32_t composed;         /* [out] groups composed ahead (dita_attn_step_ex's         */
+                            /*       compose_next), else 0                              */
 } dita_step_info;
 
 int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_list,
@@ -499,11 +501,29 @@ int dita_attn_step(dita_state_cache* cache, const void* q, const void* const* k_
  * lse may not overlap q or the K/V of any partition computed fresh, since the
  * side stream may write them while the attention reads those: DITA_ERR_ARG,
  * before anything is enqueued.
+ *
+ * Composition ahead (opts->compose_next, the next step's reuse mask; values
+ * other than 0/1: DITA_ERR_ARG before anything is enqueued).  Page section:
+ * State-Centric Parallel Runtime > Dynamic Group Compose.  After this step
+ * every partition holds a valid state, and the runs of partitions that
+ * compose_next marks reused are composed into group states exactly as
+ * dita_state_cache_compose_runs would compose them right after the step; the
+ * output is the same (the final merge reads the members, not the group).
+ * The run with the most groups is composed by the final merge itself in the
+ * same pass over the states (its group state comes from the loads of the
+ * output's merge: one pass instead of two over those states); any other run,
+ * and every run when a pre-merge is taken, by a merge of its own after the
+ * final one.  A run whose group state needs a free slot that a pooled cache
+ * lacks is left uncomposed (info->composed counts the runs composed).  The
+ * group state equals dita_state_cache_compose_runs' bit for bit when the run's
+ * first partition holds a full device slot (its state is then merged first in
+ * both), else up to the order of the fp32 sums.
  */
 typedef struct {
   void* side_stream;     /* hipStream_t for the pre-merge, or NULL                  */
   int32_t min_premerge;  /* pre-merge only with at least this many reused states   */
   int32_t reserved;      /* must be 0                                              */
+  const uint8_t* compose_next; /* host [P] reuse mask of the next step, or NULL     */
 } dita_step_opts;
 
 int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const* k_list,

@@ -63,7 +63,7 @@ class StepInfo(ctypes.Structure):
                 ("ev_begin", ctypes.c_void_p), ("ev_attn_end", ctypes.c_void_p),
                 ("ev_end", ctypes.c_void_p), ("merge_sources", ctypes.c_int32),
                 ("premerge_sources", ctypes.c_int32), ("premerge_bytes", ctypes.c_double),
-                ("fetched", ctypes.c_int32), ("reserved_out", ctypes.c_int32)]
+                ("fetched", ctypes.c_int32), ("composed", ctypes.c_int32)]
 
 
 class ErrorPlan(ctypes.Structure):
@@ -83,7 +83,7 @@ class AttnLayout(ctypes.Structure):
 
 class StepOpts(ctypes.Structure):
     _fields_ = [("side_stream", ctypes.c_void_p), ("min_premerge", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("compose_next", ctypes.POINTER(ctypes.c_uint8))]
 
 
 def _load() -> ctypes.CDLL:
@@ -551,13 +551,15 @@ class StateCache:
 
 def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reuse_mask,
                    step: int, o=None, lse=None, stream=None, events=None, side_stream=None,
-                   min_premerge: int = 0) -> StepInfo:
+                   min_premerge: int = 0, compose_next=None) -> StepInfo:
     """One rank-step: fresh states into their slots, reused slots kept, all groups merged.
 
     ``k_list``/``v_list`` hold P tensors [B,H,Nk_p,D] (entries of reused partitions may
     be None).  ``events``: optional (begin, attn_end, end) raw hipEvent_t handles.
-    ``side_stream`` (a torch stream) selects ``dita_attn_step_ex``: reused states are
-    pre-merged there while the fresh attention runs.  Returns (o, lse, StepInfo).
+    ``side_stream`` (a torch stream) and ``compose_next`` (the next step's reuse mask:
+    its runs are composed into groups by the step, the largest by the final merge
+    itself) select ``dita_attn_step_ex``; on the side stream reused states are
+    pre-merged while the fresh attention runs.  Returns (o, lse, StepInfo).
     """
     torch = _torch()
     P = cache.P
@@ -590,10 +592,18 @@ def dita_attn_step(cache: StateCache, q, k_list: Sequence, v_list: Sequence, reu
     args = (cache.handle, _ptr(q), _ptr_array([_ptr(k) for k in k_list]),
             _ptr_array([_ptr(v) for v in v_list]), nk, m, step, _ptr(o), _ptr(lse),
             _stream(q, stream))
-    if side_stream is None:
+    if side_stream is None and compose_next is None:
         _check(_lib.dita_attn_step(*args, ctypes.byref(info)), "dita_attn_step")
     else:
-        opts = StepOpts(side_stream.cuda_stream, int(min_premerge), 0)
+        nxt = None
+        if compose_next is not None:
+            nm = np.ascontiguousarray(np.asarray(compose_next, dtype=np.uint8))
+            if nm.shape != (P,):
+                raise ValueError("compose_next must have P entries")
+            nxt = (ctypes.c_uint8 * P).from_buffer_copy(nm.tobytes())
+        opts = StepOpts(side_stream.cuda_stream if side_stream is not None else None,
+                        int(min_premerge), 0,
+                        ctypes.cast(nxt, ctypes.POINTER(ctypes.c_uint8)) if nxt is not None else None)
         _check(_lib.dita_attn_step_ex(*args, ctypes.byref(opts), ctypes.byref(info)),
                "dita_attn_step_ex")
     return o, lse, info

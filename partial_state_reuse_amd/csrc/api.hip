@@ -331,19 +331,37 @@ int leaders_in(const dita_state_cache* c, int first, int last) {
 // leader on the device, no group straddling the range, and an output slot from
 // compose_output when two or more leaders take part) into one group state held
 // by `first`.
+// Cache records of a composition of first..last once its merge is enqueued
+// (out_k: the slot it wrote; -1: one leader, nothing merged): the members'
+// slots go back to the pool, `first` leads the group with the oldest stamp.
+void finish_compose(dita_state_cache* c, int first, int last, int out_k) {
+  int64_t oldest = c->stamp[first];
+  for (int p = first; p <= last; ++p)
+    if (c->group[p] == p && c->stamp[p] < oldest) oldest = c->stamp[p];
+  if (out_k >= 0) {
+    for (int p = first; p <= last; ++p) release(c, p);
+    c->phys[first] = int16_t(out_k);
+  } else {
+    for (int p = first + 1; p <= last; ++p) release(c, p);
+  }
+  for (int p = first; p <= last; ++p) {
+    c->group[p] = int16_t(first);
+    c->valid[p] = 1;
+    c->stamp[p] = oldest;
+  }
+}
+
 int compose_range(dita_state_cache* c, int first, int last, int out_k, int src0, hipStream_t stream,
                   int* launched) {
   // `first` leads its group: no group straddles the range and first is in it.
   dita::MergeSrc src{};
   int n = 0;
-  int64_t oldest = c->stamp[first];
   uint64_t touched = slot_bit(out_k);
   if (src0 >= 0) add_source(c, src, n, src0);
   for (int p = first; p <= last; ++p)
     if (c->group[p] == p) {
       if (p != src0) add_source(c, src, n, p);
       touched |= state_bit(c, p);
-      if (c->stamp[p] < oldest) oldest = c->stamp[p];
     }
   if (n > 1) {
     // In place when src0 >= 0: the output is source 0; each lane reads its
@@ -357,17 +375,44 @@ int compose_range(dita_state_cache* c, int first, int last, int out_k, int src0,
     if (st) return st;
     // The members' slots go back to the pool below: their next owner waits for this merge.
     if ((st = slots_mark(c, stream, touched))) return st;
-    for (int p = first; p <= last; ++p) release(c, p);
-    c->phys[first] = int16_t(out_k);
-  } else {
-    for (int p = first + 1; p <= last; ++p) release(c, p);
   }
-  for (int p = first; p <= last; ++p) {
-    c->group[p] = int16_t(first);
-    c->valid[p] = 1;
-    c->stamp[p] = oldest;
-  }
+  finish_compose(c, first, last, n > 1 ? out_k : -1);
   if (launched) *launched = n > 1 ? 1 : 0;
+  return DITA_OK;
+}
+
+// The runs dita_state_cache_compose_runs composes for a reuse mask: maximal
+// runs of reused partitions, shrunk to the groups that lie inside them, that
+// hold two or more groups.  DITA_ERR_ARG for mask values other than 0/1,
+// DITA_ERR_STATE for reuse of an invalid state or of a group leader that is
+// not on the device (fetch it first).
+int plan_runs(const dita_state_cache* c, const uint8_t* reuse, int* first, int* last, int* n_out) {
+  for (int p = 0; p < c->P; ++p) {
+    if (reuse[p] > 1) return DITA_ERR_ARG;
+    if (reuse[p] && !c->valid[p]) return DITA_ERR_STATE;
+  }
+  int n = 0;
+  for (int p = 0; p < c->P;) {
+    if (!reuse[p]) {
+      ++p;
+      continue;
+    }
+    int a = p, b = p;
+    while (b + 1 < c->P && reuse[b + 1]) ++b;
+    p = b + 1;
+    // Groups that reach outside the run will be recomputed whole: leave them out.
+    if (c->group[a] < a) a = group_last(c, c->group[a]) + 1;
+    if (b >= a && group_last(c, c->group[b]) > b) b = c->group[b] - 1;
+    if (a < b && !(c->group[a] == a && group_last(c, a) == b)) {
+      first[n] = a;
+      last[n] = b;
+      ++n;
+    }
+  }
+  for (int i = 0; i < n; ++i)
+    for (int p = first[i]; p <= last[i]; ++p)
+      if (c->group[p] == p && !on_device(c, p)) return DITA_ERR_STATE;
+  *n_out = n;
   return DITA_OK;
 }
 
@@ -419,7 +464,7 @@ const char* dita_status_str(int status) {
 
 int dita_last_hip_error(void) { return g_last_hip_error; }
 
-int dita_version(void) { return 112; }
+int dita_version(void) { return 113; }
 
 int dita_attn_partial(const dita_shape* shape, const void* q, const void* k, const void* v,
                       int64_t nk, void* o_p, float* lse_p, void* stream) {
@@ -750,31 +795,9 @@ int dita_state_cache_compose(dita_state_cache* cache, int first, int last, void*
 int dita_state_cache_compose_runs(dita_state_cache* cache, const uint8_t* reuse, void* stream,
                                   int* n_launched) {
   if (!cache || !reuse) return DITA_ERR_ARG;
-  for (int p = 0; p < cache->P; ++p) {
-    if (reuse[p] > 1) return DITA_ERR_ARG;
-    if (reuse[p] && !cache->valid[p]) return DITA_ERR_STATE;
-  }
   int first[DITA_MAX_PARTITIONS], last[DITA_MAX_PARTITIONS], n = 0;
-  for (int p = 0; p < cache->P;) {
-    if (!reuse[p]) {
-      ++p;
-      continue;
-    }
-    int a = p, b = p;
-    while (b + 1 < cache->P && reuse[b + 1]) ++b;
-    p = b + 1;
-    // Groups that reach outside the run will be recomputed whole: leave them out.
-    if (cache->group[a] < a) a = group_last(cache, cache->group[a]) + 1;
-    if (b >= a && group_last(cache, cache->group[b]) > b) b = cache->group[b] - 1;
-    if (a < b && !(cache->group[a] == a && group_last(cache, a) == b)) {
-      first[n] = a;
-      last[n] = b;
-      ++n;
-    }
-  }
-  for (int i = 0; i < n; ++i)
-    for (int p = first[i]; p <= last[i]; ++p)
-      if (cache->group[p] == p && !on_device(cache, p)) return DITA_ERR_STATE;  // fetch it first
+  int st0 = plan_runs(cache, reuse, first, last, &n);
+  if (st0) return st0;
   int out_k[DITA_MAX_PARTITIONS], src0[DITA_MAX_PARTITIONS];
   uint64_t taken = 0;
   for (int i = 0; i < n; ++i) {
@@ -875,6 +898,10 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
   if (opts && (opts->reserved != 0 || opts->min_premerge < 0)) return DITA_ERR_ARG;
   const dita_shape& s = cache->shape;
   const int P = cache->P;
+  const uint8_t* compose_next = opts ? opts->compose_next : nullptr;
+  if (compose_next)
+    for (int p = 0; p < P; ++p)
+      if (compose_next[p] > 1) return DITA_ERR_ARG;
   const size_t ob = cache->o_bytes, lb = state_lse_bytes(s);
   if (overlaps(o, ob, cache->base, cache->bytes) || overlaps(lse, lb, cache->base, cache->bytes) ||
       overlaps(q, ob, cache->base, cache->bytes) || overlaps(o, ob, lse, lb))
@@ -1010,13 +1037,63 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     ++n_src;
     src_bytes += double(ob + lb);
   }
+  // Composition ahead: after this step every partition holds a valid state on
+  // the device, so the runs the next step reuses can be composed now.  The
+  // largest run is composed by the final merge itself (its leaders are
+  // consecutive sources there, and the group state comes from the same loads);
+  // the others, and every run after a pre-merge, by merges of their own after
+  // it.  A run whose group state would need a free slot that a pooled cache
+  // lacks is left as it is.
+  int run_first[DITA_MAX_PARTITIONS], run_last[DITA_MAX_PARTITIONS], n_runs = 0;
+  int fused = -1, fused_out = -1, fused_src0 = -1;
+  uint64_t taken_runs = taken;
+  if (compose_next) {
+    if ((st = plan_runs(cache, compose_next, run_first, run_last, &n_runs))) return st;
+    int most = 1;
+    for (int i = 0; i < n_runs && !premerge; ++i) {
+      const int l = leaders_in(cache, run_first[i], run_last[i]);
+      if (l > most) {
+        most = l;
+        fused = i;
+      }
+    }
+    if (fused >= 0 &&
+        (fused_out = compose_output(cache, run_first[fused], run_last[fused], &taken_runs,
+                                    &fused_src0)) < 0)
+      fused = -1;
+  }
+  dita::MergeGroup group{};
   for (int p = 0; p < P; ++p) {
     if (cache->group[p] != p || (premerge && reuse[p])) continue;
     src_bytes += cache->cphys[p] >= 0 ? compact_bytes : double(ob + lb);
+    if (fused >= 0 && p == run_first[fused]) group.first = n_src;
     add_source(cache, src, n_src, p);
+    if (fused >= 0 && p <= run_last[fused]) group.end = n_src;
   }
-  if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_src, src, o, lse, hs)))) return st;
+  if (fused >= 0) {
+    group.o = phys_o(cache, fused_out);
+    group.lse = phys_lse(cache, fused_out);
+    // A group state written out of place goes to a slot from the pool.
+    if ((st = slots_wait(cache, hs, slot_bit(fused_out)))) return st;
+    touched |= slot_bit(fused_out);
+  }
+  if ((st = hip_status(dita::launch_merge(s.dtype, s.D, rows, n_src, src, o, lse, hs, group))))
+    return st;
   if ((st = slots_mark(cache, hs, touched))) return st;
+  int composed = 0;
+  if (fused >= 0) {
+    finish_compose(cache, run_first[fused], run_last[fused], fused_out);
+    ++composed;
+  }
+  for (int i = 0; i < n_runs; ++i) {
+    if (i == fused) continue;
+    int out_k = -1, src0 = -1;
+    if (leaders_in(cache, run_first[i], run_last[i]) > 1 &&
+        (out_k = compose_output(cache, run_first[i], run_last[i], &taken_runs, &src0)) < 0)
+      continue;
+    if ((st = compose_range(cache, run_first[i], run_last[i], out_k, src0, hs, nullptr))) return st;
+    ++composed;
+  }
   if (info && info->ev_end && (st = hip_status(hipEventRecord(static_cast<hipEvent_t>(info->ev_end), hs))))
     return st;
   if (info) {
@@ -1024,14 +1101,15 @@ int dita_attn_step_ex(dita_state_cache* cache, const void* q, const void* const*
     info->n_reused = P - n_fresh;
     info->fresh_flops = 4.0 * double(s.B) * s.H * double(s.Nq) * fresh_keys * s.D;
     info->merge_sources = n_src;
-    info->merge_bytes = src_bytes + double(ob + lb);
+    // The output, and the group state the final merge composed, if any.
+    info->merge_bytes = src_bytes + double(ob + lb) * (fused >= 0 ? 2.0 : 1.0);
     info->premerge_sources = premerge ? n_reused_heads : 0;
     double pre_bytes = double(ob + lb);
     for (int i = 0; i < n_reused_heads; ++i)
       pre_bytes += cache->cphys[reused_heads[i]] >= 0 ? compact_bytes : double(ob + lb);
     info->premerge_bytes = premerge ? pre_bytes : 0.0;
     info->fetched = n_fetch;
-    info->reserved_out = 0;
+    info->composed = composed;
   }
   return DITA_OK;
 }

@@ -60,9 +60,18 @@ struct MergeSrc {
   const float* scale[kMaxParts];
 };
 
+// Optional second output of a merge: the merge of sources [first, end) alone
+// (a group state composed in the same pass), written to (o, lse).  o may be
+// the output of source `first` (in place).  end <= first: none.
+struct MergeGroup {
+  int first, end;
+  void* o;
+  float* lse;
+};
+
 // P-way LSE merge over `rows` = B*H*Nq rows of D elements.  dtype: 0 fp32, 1 bf16.
 hipError_t launch_merge(int dtype, int D, int64_t rows, int P, const MergeSrc& src, void* o,
-                        float* lse, hipStream_t stream);
+                        float* lse, hipStream_t stream, const MergeGroup& group = MergeGroup{});
 
 struct LseList {
   const float* lse[kMaxParts];

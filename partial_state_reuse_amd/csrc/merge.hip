@@ -88,9 +88,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 // src.scale[j] one fp32 scale per row; their values are code * scale (one
 // fp32 product, as the encoding defines).  The lane reads 8 code bytes and the
 // row's scale instead of its 16-byte chunk.
-template <typename T, int D, bool COMPACT>
+//
+// GROUP: the merge of sources [g.first, g.end) alone goes to (g.o, g.lse) as
+// well, from the same loads, with the operations of a merge of those sources
+// by themselves in the same order (the same bits as that merge).  g.o may be
+// source g.first's output (in place, as above).
+template <typename T, int D, bool COMPACT, bool GROUP>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, int64_t rows,
-                                                         uint64_t compact, T* o, float* lse) {
+                                                         uint64_t compact, T* o, float* lse,
+                                                         MergeGroup g) {
   constexpr int VN = Vec<T>::N;
   constexpr int LPR = D / VN;          // lanes per row
   constexpr int RPB = kThreads / LPR;  // rows per block
@@ -125,19 +131,44 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
   for (int j = 0; j < kChunk; ++j)
     if (j < P) M = fmaxf(M, lp[j]);
   for (int p = kChunk; p < P; ++p) M = fmaxf(M, src.lse[p][row]);
-
-  float acc[VN];
+  auto in_group = [&](int p) { return GROUP && p >= g.first && p < g.end; };
+  float M2 = -INFINITY;
+  if constexpr (GROUP) {
 #pragma unroll
-  for (int i = 0; i < VN; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < kChunk; ++j)
+      if (j < P && in_group(j)) M2 = fmaxf(M2, lp[j]);
+    for (int p = kChunk; p < P; ++p)
+      if (in_group(p)) M2 = fmaxf(M2, src.lse[p][row]);
+  }
+
+  float acc[VN], acc2[VN];
+#pragma unroll
+  for (int i = 0; i < VN; ++i) acc[i] = acc2[i] = 0.0f;
+  // The group's state, written after every load of the row (in place safe).
+  auto store_group = [&](float L2) {
+    if constexpr (GROUP) {
+      if (M2 == -INFINITY) {
+        *reinterpret_cast<u32x4*>(static_cast<T*>(g.o) + off) = Vec<T>::pack(acc2);
+        if (c == 0) g.lse[row] = -INFINITY;
+        return;
+      }
+      const float inv2 = 1.0f / L2;
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc2[i] *= inv2;
+      *reinterpret_cast<u32x4*>(static_cast<T*>(g.o) + off) = Vec<T>::pack(acc2);
+      if (c == 0) g.lse[row] = M2 + __builtin_amdgcn_logf(L2) * kLn2;
+    }
+  };
   if (M == -INFINITY) {
     *reinterpret_cast<u32x4*>(o + off) = Vec<T>::pack(acc);
     if (c == 0) lse[row] = -INFINITY;
+    store_group(0.0f);  // M2 is -inf too
     return;
   }
   // w_p = exp(LSE_p - M) = exp2((LSE_p - M) log2 e); 0 for LSE_p = -inf.  The
   // difference is taken first, so the largest state weighs exactly 1 (a
   // one-state merge returns its input unchanged).
-  float L = 0.0f;
+  float L = 0.0f, L2 = 0.0f;
   auto accumulate = [&](int j, int p) {
     const float w = __builtin_amdgcn_exp2f((lp[j] - M) * kLog2e);
     L += w;
@@ -153,6 +184,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
     }
 #pragma unroll
     for (int i = 0; i < VN; ++i) acc[i] = __builtin_fmaf(w, x[i], acc[i]);
+    if (in_group(p)) {
+      const float w2 = __builtin_amdgcn_exp2f((lp[j] - M2) * kLog2e);
+      L2 += w2;
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc2[i] = __builtin_fmaf(w2, x[i], acc2[i]);
+    }
   };
 #pragma unroll
   for (int j = 0; j < kChunk; ++j)
@@ -171,11 +208,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeSrc src, int P, in
   for (int i = 0; i < VN; ++i) acc[i] *= inv;
   *reinterpret_cast<u32x4*>(o + off) = Vec<T>::pack(acc);
   if (c == 0) lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;  // hardware log2; L >= 1
+  store_group(L2);
 }
 
-template <typename T, int D>
-hipError_t launch_merge_t(int64_t rows, int P, const MergeSrc& src, void* o, float* lse,
-                          hipStream_t stream) {
+template <typename T, int D, bool GROUP>
+hipError_t launch_merge_g(int64_t rows, int P, const MergeSrc& src, void* o, float* lse,
+                          hipStream_t stream, const MergeGroup& g) {
   constexpr int LPR = D / Vec<T>::N;
   constexpr int RPB = kThreads / LPR;
   const int64_t blocks = (rows + RPB - 1) / RPB;
@@ -184,14 +222,21 @@ hipError_t launch_merge_t(int64_t rows, int P, const MergeSrc& src, void* o, flo
     if (src.scale[p]) compact |= uint64_t(1) << p;
   if constexpr (sizeof(T) == 2) {
     if (compact) {
-      merge_kernel<T, D, true><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(
-          src, P, rows, compact, static_cast<T*>(o), lse);
+      merge_kernel<T, D, true, GROUP><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(
+          src, P, rows, compact, static_cast<T*>(o), lse, g);
       return hipGetLastError();
     }
   }
-  merge_kernel<T, D, false><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(src, P, rows, 0,
-                                                                             static_cast<T*>(o), lse);
+  merge_kernel<T, D, false, GROUP><<<dim3(unsigned(blocks)), kThreads, 0, stream>>>(
+      src, P, rows, 0, static_cast<T*>(o), lse, g);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_merge_t(int64_t rows, int P, const MergeSrc& src, void* o, float* lse,
+                          hipStream_t stream, const MergeGroup& g) {
+  if (g.end > g.first) return launch_merge_g<T, D, true>(rows, P, src, o, lse, stream, g);
+  return launch_merge_g<T, D, false>(rows, P, src, o, lse, stream, g);
 }
 
 __global__ __launch_bounds__(kThreads) void copy_state_kernel(const u32x4* __restrict__ so,
@@ -207,13 +252,16 @@ __global__ __launch_bounds__(kThreads) void copy_state_kernel(const u32x4* __res
 }  // namespace
 
 hipError_t launch_merge(int dtype, int D, int64_t rows, int P, const MergeSrc& src, void* o,
-                        float* lse, hipStream_t stream) {
+                        float* lse, hipStream_t stream, const MergeGroup& group) {
+  if (group.end > group.first &&
+      (group.first < 0 || group.end > P || !group.o || !group.lse))
+    return hipErrorInvalidValue;
   if (dtype == 1) {
-    return D == 128 ? launch_merge_t<__bf16, 128>(rows, P, src, o, lse, stream)
-                    : launch_merge_t<__bf16, 64>(rows, P, src, o, lse, stream);
+    return D == 128 ? launch_merge_t<__bf16, 128>(rows, P, src, o, lse, stream, group)
+                    : launch_merge_t<__bf16, 64>(rows, P, src, o, lse, stream, group);
   }
-  return D == 128 ? launch_merge_t<float, 128>(rows, P, src, o, lse, stream)
-                  : launch_merge_t<float, 64>(rows, P, src, o, lse, stream);
+  return D == 128 ? launch_merge_t<float, 128>(rows, P, src, o, lse, stream, group)
+                  : launch_merge_t<float, 64>(rows, P, src, o, lse, stream, group);
 }
 
 hipError_t launch_copy_state(const void* src_o, const float* src_lse, void* dst_o, float* dst_lse,

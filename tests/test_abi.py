@@ -293,6 +293,11 @@ def test_attn_step_ex_validates_options():
     opts = dita.StepOpts(FAKE_DEV, 0, 0)
     assert lib.dita_attn_step_ex(h, q, ks, ks, nk, (ctypes.c_uint8 * 2)(0, 1), 0, o, l, None,
                                  ctypes.byref(opts), None) == dita.DITA_ERR_STATE
+    # compose_next holds 0/1 values only: rejected before anything is enqueued
+    bad = (ctypes.c_uint8 * 2)(0, 2)
+    opts = dita.StepOpts(None, 0, 0, ctypes.cast(bad, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.dita_attn_step_ex(h, q, ks, ks, nk, zeros, 0, o, l, None, ctypes.byref(opts),
+                                 None) == dita.DITA_ERR_ARG
     lib.dita_state_cache_free(h)
 
 

@@ -232,3 +232,48 @@ def test_premerge_schedule_matches_oracle_and_one_stream(dev, dtype, D):
 def test_compose_ahead_schedule_matches_oracle(dev, side):
     say(f"[compose-ahead schedule side={side}]")
     _run_schedule(dev, "bf16", 128, side, schedule=_compose_ahead_schedule(12, 6, seed=3))
+
+
+@pytest.mark.parametrize("pooled", [False, True])
+def test_step_composes_ahead_like_compose_runs(dev, pooled):
+    """dita_attn_step_ex with compose_next: the step composes the next step's
+    reused runs itself, the largest one in the same pass as its final merge.
+    Against the plain step followed by compose_runs on a second cache, over a
+    schedule with two runs per reuse step (one fused into the merge, one merged
+    on its own) and an all-fresh step in between: outputs, group ranges and
+    group states bit for bit (the runs start at partitions that hold full
+    slots), and the count of composed runs."""
+    import torch
+    import partial_state_reuse_amd as dita
+    H, nq, D, P, n = 4, 300, 128, 8, 260
+    rng = np.random.default_rng(11 + pooled)
+    q, ks, vs = _inputs(rng, H, nq, [n] * P, D, "bf16")
+    tq = to_dev(q, "bf16", dev)
+    fresh = np.zeros(P, np.uint8)
+    near = np.array([1, 1, 0, 0, 0, 1, 1, 1], np.uint8)  # runs [0, 1] and [5, 7]
+    masks = [fresh, near, near, fresh, near, near]
+    slots = P if pooled else None
+    a = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=slots)
+    b = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev, slots=slots)
+    for s, mask in enumerate(masks):
+        nxt = masks[s + 1] if s + 1 < len(masks) else None
+        tk = [to_dev(x, "bf16", dev) for x in ks]
+        tv = [to_dev(x, "bf16", dev) for x in vs]
+        oa, la, ia = dita.dita_attn_step(a, tq, tk, tv, mask, s, compose_next=nxt)
+        ob, lb, _ = dita.dita_attn_step(b, tq, tk, tv, mask, s)
+        runs = b.compose_runs(nxt) if nxt is not None else 0
+        torch.cuda.synchronize()
+        say(f"  step {s} pooled={pooled}: composed {ia.composed}, compose_runs launched {runs}")
+        assert np.array_equal(to_host(oa), to_host(ob)) and np.array_equal(to_host(la), to_host(lb)), s
+        assert ia.composed == (2 if nxt is not None and (mask == 0).all() else 0), (s, ia.composed)
+        for p in range(P):
+            assert a.group(p) == b.group(p), (s, p, a.group(p), b.group(p))
+            assert a.info(p) == b.info(p), (s, p)
+        for p in range(P):
+            if a.group(p)[0] != p:
+                continue
+            so, sl = a.slot(p)
+            ro, rl = b.slot(p)
+            assert np.array_equal(to_host(so), to_host(ro)) and np.array_equal(to_host(sl), to_host(rl)), (s, p)
+        ks = _drift(rng, ks, "bf16")
+        vs = _drift(rng, vs, "bf16")
