@@ -282,44 +282,50 @@ def test_grouped_launch_with_256_row_tiles(dev, D):
 # device: every 512-row tile first, then every 256-row tile, with some pairs
 # holding one 512-row tile fewer and two 256-row tiles more (or, last case,
 # 256-row tiles only).
-STAGED_CASES = [(24, 1100, 6, 300, 128), (41, 1300, 5, 300, 64), (12, 1800, 8, 300, 64),
-                (8, 1000, 1, 700, 128)]
+# (B, H, nq, P, nk, D); the B = 2 case decodes pairs through B * H.
+STAGED_CASES = [(1, 24, 1100, 6, 300, 128), (1, 41, 1300, 5, 300, 64), (1, 12, 1800, 8, 300, 64),
+                (1, 8, 1000, 1, 700, 128), (2, 12, 1100, 6, 300, 128)]
 
 
-@pytest.mark.parametrize("H,nq,P,nk,D", STAGED_CASES)
-def test_grouped_launch_with_staged_tiles(dev, H, nq, P, nk, D):
+@pytest.mark.parametrize("B,H,nq,P,nk,D", STAGED_CASES)
+def test_grouped_launch_with_staged_tiles(dev, B, H, nq, P, nk, D):
     """A grouped launch in the staged layout: the library's layout says so, its
     tile counts add up to the grid, and every head and row of the step output
     and of every fresh state matches the oracle."""
     import torch
     import partial_state_reuse_amd as dita
     from gpu_util import HeadChunkedOracle
-    lay = dita.dita_attn_launch_info(1, H, nq, D, P, nk)
-    say(f"staged tiles H={H} nq={nq} P={P} nk={nk} D={D} layout={lay}")
+    lay = dita.dita_attn_launch_info(B, H, nq, D, P, nk)
+    say(f"staged tiles B={B} H={H} nq={nq} P={P} nk={nk} D={D} layout={lay}")
     if lay["compute_units"] != 256:
         pytest.skip("layout chosen for a 256-CU device")
-    pairs = H * P
+    pairs = B * H * P
     a = lay["staged_pairs"]
     assert 0 <= a <= pairs and lay["split_units"] == 0 and lay["dual_tails"] == 0, lay
     n_big = a * lay["big_tiles"] + (pairs - a) * (lay["big_tiles"] - 1)
     n_small = a * lay["small_tiles"] + (pairs - a) * lay["small_tiles_b"]
     assert n_small > 0 and lay["workgroups"] == n_big + n_small, lay
-    rng = np.random.default_rng(H * 37 + nq + P + D)
-    q = round_bf16(rng.standard_normal((1, H, nq, D)).astype(np.float32) * 1.5)
-    ks = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 1.5) for _ in range(P)]
-    vs = [round_bf16(rng.standard_normal((1, H, nk, D)).astype(np.float32) * 0.35) for _ in range(P)]
-    cache = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    rng = np.random.default_rng(B * 1009 + H * 37 + nq + P + D)
+    q = round_bf16(rng.standard_normal((B, H, nq, D)).astype(np.float32) * 1.5)
+    ks = [round_bf16(rng.standard_normal((B, H, nk, D)).astype(np.float32) * 1.5) for _ in range(P)]
+    vs = [round_bf16(rng.standard_normal((B, H, nk, D)).astype(np.float32) * 0.35) for _ in range(P)]
+    cache = dita.StateCache(B, H, nq, D, torch.bfloat16, P, device=dev)
     fresh = np.zeros(P, np.uint8)
     o, lse, info = dita.dita_attn_step(cache, to_dev(q, "bf16", dev), [to_dev(x, "bf16", dev) for x in ks],
                                        [to_dev(x, "bf16", dev) for x in vs], fresh, 0)
     assert info.n_fresh == P
-    ref = HeadChunkedOracle(P, H, chunk=max(1, H // 16))
-    o_ref, lse_ref, _ = ref.step(q, ks, vs, fresh, 0)
-    assert_state_close(to_host(o), to_host(lse), o_ref, lse_ref, "bf16", "staged tiles, output")
-    for p in range(P):
-        so, sl = cache.slot(p)
-        ro, rl = ref.slot(p)
-        assert_state_close(to_host(so), to_host(sl), ro, rl, "bf16", f"staged tiles, state {p}")
+    o_h, l_h = to_host(o), to_host(lse)
+    slots = [tuple(to_host(t) for t in cache.slot(p)) for p in range(P)]
+    for b in range(B):  # the head-chunked oracle takes one batch entry at a time
+        ref = HeadChunkedOracle(P, H, chunk=max(1, H // 16))
+        o_ref, lse_ref, _ = ref.step(q[b:b + 1], [x[b:b + 1] for x in ks], [x[b:b + 1] for x in vs],
+                                     fresh, 0)
+        assert_state_close(o_h[b:b + 1], l_h[b:b + 1], o_ref, lse_ref, "bf16",
+                           f"staged tiles, output, batch {b}")
+        for p in range(P):
+            ro, rl = ref.slot(p)
+            assert_state_close(slots[p][0][b:b + 1], slots[p][1][b:b + 1], ro, rl, "bf16",
+                               f"staged tiles, state {p}, batch {b}")
 
 DUAL_CASES = [(40, 600, 8, 700, 128), (41, 600, 7, 700, 128), (40, 2100, 8, 700, 64)]
 
