@@ -277,3 +277,47 @@ def test_step_composes_ahead_like_compose_runs(dev, pooled):
             assert np.array_equal(to_host(so), to_host(ro)) and np.array_equal(to_host(sl), to_host(rl)), (s, p)
         ks = _drift(rng, ks, "bf16")
         vs = _drift(rng, vs, "bf16")
+
+
+def test_step_composes_ahead_with_premerge(dev):
+    """compose_next together with the side-stream pre-merge: on steps that
+    pre-merge their reused states the runs are composed by merges of their own
+    after the final merge, on all-fresh steps by the final merge itself.
+    Against the same two-stream step followed by compose_runs: outputs, group
+    ranges and group states bit for bit, and the count of composed runs."""
+    import torch
+    import partial_state_reuse_amd as dita
+    H, nq, D, P, n = 4, 300, 128, 8, 260
+    rng = np.random.default_rng(23)
+    q, ks, vs = _inputs(rng, H, nq, [n] * P, D, "bf16")
+    tq = to_dev(q, "bf16", dev)
+    fresh = np.zeros(P, np.uint8)
+    m_a = np.array([1, 1, 0, 0, 0, 0, 1, 0], np.uint8)  # reused: group [0, 1] and 6
+    m_b = np.array([1, 1, 0, 0, 0, 1, 1, 1], np.uint8)  # then also 5 and 7: run [5, 7]
+    masks = [fresh, m_a, m_b, fresh, m_a, m_b]
+    want = [1, 1, 0, 1, 1, 0]  # runs composed: [0, 1]; [5, 7]; none; ...
+    side = torch.cuda.Stream(device=dev)
+    a = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    b = dita.StateCache(1, H, nq, D, torch.bfloat16, P, device=dev)
+    for s, mask in enumerate(masks):
+        nxt = masks[s + 1] if s + 1 < len(masks) else None
+        tk = [to_dev(x, "bf16", dev) for x in ks]
+        tv = [to_dev(x, "bf16", dev) for x in vs]
+        oa, la, ia = dita.dita_attn_step(a, tq, tk, tv, mask, s, side_stream=side, compose_next=nxt)
+        ob, lb, ib = dita.dita_attn_step(b, tq, tk, tv, mask, s, side_stream=side)
+        if nxt is not None:
+            b.compose_runs(nxt)
+        torch.cuda.synchronize()
+        say(f"  step {s}: premerged {ia.premerge_sources}, composed {ia.composed}")
+        assert ia.premerge_sources == ib.premerge_sources, s
+        assert np.array_equal(to_host(oa), to_host(ob)) and np.array_equal(to_host(la), to_host(lb)), s
+        assert ia.composed == want[s], (s, ia.composed)
+        for p in range(P):
+            assert a.group(p) == b.group(p), (s, p, a.group(p), b.group(p))
+            assert a.info(p) == b.info(p), (s, p)
+            if a.group(p)[0] == p:
+                so, sl = a.slot(p)
+                ro, rl = b.slot(p)
+                assert np.array_equal(to_host(so), to_host(ro)) and np.array_equal(to_host(sl), to_host(rl)), (s, p)
+        ks = _drift(rng, ks, "bf16")
+        vs = _drift(rng, vs, "bf16")
