@@ -412,6 +412,21 @@ def sustained_clock(run_step, seconds: float = 4.0):
                    "2.5 PFLOP/s x clock / 2.4 GHz"}
 
 
+def attn_by_blocks(attn_ms, infos):
+    """The attention launches of the timed steps grouped by their fresh-block count:
+    launches, mean ms and TFLOP/s per group (the anchor steps' launches differ in
+    shape from the others)."""
+    groups = {}
+    for ms, info in zip(attn_ms, infos):
+        if info.n_fresh > 0:
+            g = groups.setdefault(str(info.n_fresh), [0, 0.0, 0.0])
+            g[0] += 1
+            g[1] += ms
+            g[2] += info.fresh_flops
+    return {k: {"launches": n, "ms_mean": t / n, "TFLOPs": f / (t / 1e3) / 1e12}
+            for k, (n, t, f) in sorted(groups.items(), key=lambda kv: int(kv[0]))}
+
+
 def _call_times(dita, stream, call, reps: int):
     """GPU time of each of `reps` calls made back to back on `stream`: one call is
     queued ahead of the first event, so the host's launch work for each call
@@ -787,6 +802,7 @@ def main():
         "step_ms": [round(x, 4) for x in step_ms],
         "step_ms_median": float(np.median(step_ms)),
         "step_ms_min": float(np.min(step_ms)),
+        "attn_by_fresh_blocks": attn_by_blocks(attn_ms, infos),
         "roofline": {
             "kernel": "attn_fwd_bf16_kernel (grouped fresh partial attention)"
             if wl.dtype == "bf16" else "attn_fwd_f32_kernel",
