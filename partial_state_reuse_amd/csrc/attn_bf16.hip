@@ -347,23 +347,24 @@ constexpr int kCoherent = 16;  // buffer cache policy: sc1 (agent scope)
 __device__ inline uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ inline float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// The tile's output from its n pieces (2 <= n <= kMaxPieces) in scratch slots
+// The tile's output from its n pieces (2 <= n <= NP) in scratch slots
 // slot[0 .. n-1] (key order): weights from the pieces' running maxima, then
 // per 16-byte group of accumulators the weighted sum, normalised, rounded to
-// bf16 and stored; the loads of four groups of all pieces are issued before
-// any is used.
-template <int D>
+// bf16 and stored; the loads of G groups of all pieces are issued before any
+// is used (the registers of a batch hold G * NP groups; G divides the 16
+// groups of a lane's accumulators).
+template <int D, int NP, int G>
 __device__ __forceinline__ void split_combine(__amdgpu_buffer_rsrc_t rs, const uint32_t (&slot)[kMaxPieces],
                                               int n, int wave, int lane, const int (&qrow)[2], int Nq,
                                               __bf16* o_head, float* lse_head) {
   using T = Tile<D, 2>;
   constexpr int ND = D / 32;
-  constexpr int G = 4;  // 16-byte groups per batch of loads
+  static_assert(NP <= kMaxPieces, "pieces");
   const uint32_t lane_off = uint32_t(lane) * 16;
   const uint32_t stats_off = uint32_t(T::PIECE_O + wave * 1024) + lane_off;
-  float ms[kMaxPieces][2], ls[kMaxPieces][2];
+  float ms[NP][2], ls[NP][2];
 #pragma unroll
-  for (int i = 0; i < kMaxPieces; ++i) {
+  for (int i = 0; i < NP; ++i) {
     ms[i][0] = ms[i][1] = -INFINITY;
     ls[i][0] = ls[i][1] = 0.0f;
     if (i < n) {
@@ -378,13 +379,13 @@ __device__ __forceinline__ void split_combine(__amdgpu_buffer_rsrc_t rs, const u
   for (int qb = 0; qb < 2; ++qb) {
     float mx = ms[0][qb];
 #pragma unroll
-    for (int i = 1; i < kMaxPieces; ++i) mx = fmaxf(mx, ms[i][qb]);
-    float w[kMaxPieces];
+    for (int i = 1; i < NP; ++i) mx = fmaxf(mx, ms[i][qb]);
+    float w[NP];
 #pragma unroll
-    for (int i = 0; i < kMaxPieces; ++i) w[i] = __builtin_amdgcn_exp2f(ms[i][qb] - mx);
+    for (int i = 0; i < NP; ++i) w[i] = __builtin_amdgcn_exp2f(ms[i][qb] - mx);
     float l = w[0] * ls[0][qb];
 #pragma unroll
-    for (int i = 1; i < kMaxPieces; ++i)
+    for (int i = 1; i < NP; ++i)
       if (i < n) l = __builtin_fmaf(w[i], ls[i][qb], l);
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = 1.0f / l_tot;
@@ -392,9 +393,9 @@ __device__ __forceinline__ void split_combine(__amdgpu_buffer_rsrc_t rs, const u
     __bf16* __restrict__ op = o_head + int64_t(valid ? qrow[qb] : 0) * D;
     const uint32_t base = uint32_t(((wave * 2 + qb) * ND * 4) * 64 * 16) + lane_off;
     for (int c0 = 0; c0 < ND * 4; c0 += G) {
-      u32x4 x[G][kMaxPieces];
+      u32x4 x[G][NP];
 #pragma unroll
-      for (int i = 0; i < kMaxPieces; ++i)
+      for (int i = 0; i < NP; ++i)
         if (i < n) {
 #pragma unroll
           for (int g = 0; g < G; ++g)
@@ -407,7 +408,7 @@ __device__ __forceinline__ void split_combine(__amdgpu_buffer_rsrc_t rs, const u
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = w[0] * u2f(x[g][0][e]);
 #pragma unroll
-        for (int i = 1; i < kMaxPieces; ++i)
+        for (int i = 1; i < NP; ++i)
           if (i < n) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w[i], u2f(x[g][i][e]), acc[e]);
@@ -503,7 +504,9 @@ __device__ __forceinline__ void split_piece(const f32x16 (&oacc)[2][D / 32], con
   uint32_t slot[kMaxPieces];
 #pragma unroll
   for (int i = 0; i < kMaxPieces; ++i) slot[i] = slot_base(first + (i < n ? i : 0));
-  split_combine<D>(rs, slot, n, wave, lane, qrow, Nq, o_head, lse_head);
+  // Two 16-byte groups of every piece per batch of loads: a batch of all
+  // kMaxPieces pieces then holds 64 registers (four groups spill).
+  split_combine<D, kMaxPieces, 2>(rs, slot, n, wave, lane, qrow, Nq, o_head, lse_head);
 }
 
 // One query tile: QB * 256 query rows from row0 of head bh against job jid's
@@ -1170,8 +1173,8 @@ SplitPlan choose_key_split(int64_t n, int cus, int T, double t_tiles) {
   if (T < 2 || rem == 0) return none;  // unequal key lengths (T = 0), one key tile, whole rounds
   // Early reject by the split's best case (the most units, hence the shortest
   // ranges) before the planner checks every tile's pieces.
-  const int64_t most_units = std::min<int64_t>(std::min(cus, kSplitMaxUnits),
-                                               rem * std::min(kSplitMaxUnitsPerTile, T));
+  const int per_tile = std::max(4, std::min(kSplitMaxUnitsPerTile, T / kSplitMinIters));
+  const int64_t most_units = std::min<int64_t>(std::min(cus, kSplitMaxUnits), rem * std::min(per_tile, T));
   if (most_units <= rem) return none;
   const double best = double(n / cus) * (1.0 + kRoundSpread) +
                       kSplitIterCost * double((rem * T + most_units - 1) / most_units +

@@ -69,8 +69,13 @@ constexpr bool split_has_second(const SplitPlan& p, int64_t u) {
 
 // Host planning limits.
 constexpr int kSplitMaxUnits = 256;                 // units per launch
-constexpr int kSplitMaxPieces = 5;                  // pieces of one tile
-constexpr int kSplitMaxUnitsPerTile = 4;            // a unit covers at least a quarter tile
+constexpr int kSplitMaxPieces = 8;                  // pieces of one tile
+constexpr int kSplitMaxUnitsPerTile = 6;            // a unit covers at least a sixth of a tile
+// More than 4 units per tile only where each still gets at least this many key
+// tiles: a unit's fixed costs (its Q tile, the pipeline's restart, storing its
+// piece and the combination reading one more) outweigh shorter ranges
+// (measured: 4725 x 2000 keys, 30 heads, 7 pieces a tile: 9% slower than 4).
+constexpr int kSplitMinIters = 40;
 constexpr int kSplitMaxCounters = 4096;             // remainder tiles per launch
 
 // Key split of the last round of n tiles with T key-tile iterations each on
@@ -78,15 +83,16 @@ constexpr int kSplitMaxCounters = 4096;             // remainder tiles per launc
 // iterations of overhead per segment.  Returns the plan (units == 0: no
 // split) and its estimated finishing time in tile times (*t_est): the whole
 // rounds, then one unit's range in two segments.  More units than remainder
-// tiles, so a unit's range is shorter than a tile; at most kSplitMaxPieces
-// pieces per tile.
+// tiles, so a unit's range is shorter than a tile; 4 units per tile at most,
+// up to kSplitMaxUnitsPerTile for long key ranges (kSplitMinIters), and at
+// most kSplitMaxPieces pieces per tile.
 inline SplitPlan plan_key_split(int64_t n, int cus, int T, int segment_cost, double* t_est) {
   SplitPlan none{};
   if (cus < 1 || T < 2) return none;
   const int64_t rem = n % cus;
   if (rem == 0 || rem > kSplitMaxCounters) return none;
-  const int64_t top = std::min<int64_t>(std::min(cus, kSplitMaxUnits),
-                                        rem * std::min(kSplitMaxUnitsPerTile, T));
+  const int per_tile = std::max(4, std::min(kSplitMaxUnitsPerTile, T / kSplitMinIters));
+  const int64_t top = std::min<int64_t>(std::min(cus, kSplitMaxUnits), rem * std::min(per_tile, T));
   for (int64_t U = top; U > rem; --U) {
     SplitPlan c{};
     c.units = int(U);
