@@ -148,3 +148,31 @@ def test_step_invariants(dev, name):
     assert bool((o3 == o2).all()) and bool((l3 == l2).all()), "all-reuse changed the output"
     for p in range(wl.P):
         assert cache.info(p) == (True, 2)
+
+
+def test_dit75k_lone_block_partial(dev):
+    """One dita_attn_partial call on one 75,600-token block (the rank's 4725
+    queries against partition 5's 4725 keys, all 40 heads), the launch the
+    planner lays out staged on a 256-CU device (255 512-row tiles, then 250
+    256-row tiles): all heads at rows reaching every query block and tile,
+    against the oracle's partial state."""
+    import partial_state_reuse_amd as dita
+    from oracle import partial_state
+    wl = workloads.get("dit75k_bf16")
+    lay = dita.dita_attn_launch_info(wl.B, wl.H, wl.Nq, wl.D, 1, wl.Nk)
+    say(f"[{wl.name}] lone block layout={lay}")
+    if lay["compute_units"] == 256:
+        assert lay["staged_pairs"] >= 0 and lay["split_units"] == 0, lay
+    inp = Inputs(wl, seed=3)
+    k, v = inp.kv(0)
+    a, b = wl.part_range(5)
+    kp, vp = np.ascontiguousarray(k[:, :, a:b]), np.ascontiguousarray(v[:, :, a:b])
+    del k, v
+    o, lse = dita.dita_attn_partial(to_dev(inp.q, wl.dtype, dev), to_dev(kp, wl.dtype, dev),
+                                    to_dev(vp, wl.dtype, dev))
+    rows = covering_rows(wl.Nq)
+    o_ref, lse_ref = partial_state(np.ascontiguousarray(inp.q[:, :, rows]), kp, vp)
+    import torch
+    rows_t = torch.from_numpy(rows).to(dev)
+    assert_state_close(to_host(o.index_select(2, rows_t)), to_host(lse.index_select(2, rows_t)),
+                       o_ref, lse_ref, wl.dtype, "lone 75,600-token block")
