@@ -42,7 +42,9 @@ def sample_rows(wl):
 def run_schedule(wl, dev, steps=None, seed=0, compose_ahead=False):
     """Run the workload's schedule on both sides.  With ``compose_ahead`` the
     runs of partitions the next step reuses are composed into groups after
-    every step (the benchmark's default pipeline), on both sides."""
+    every step, on both sides: by ``compose_runs`` after the step, or with
+    ``compose_ahead="step"`` by the step itself (``compose_next``, the
+    benchmark's pipeline; the oracle composes after its step)."""
     import torch
     import partial_state_reuse_amd as dita
     steps = wl.steps if steps is None else steps
@@ -72,7 +74,10 @@ def run_schedule(wl, dev, steps=None, seed=0, compose_ahead=False):
         ref_m = oracle_mask(ref_plan, s, ref_cache.valid)
         assert np.array_equal(mask, ref_m), (s, mask, ref_m)
         ks, vs = partition_tensors(k, wl, dev), partition_tensors(v, wl, dev)
-        o, lse, info = dita.dita_attn_step(cache, q_dev, ks, vs, mask, s)
+        # every partition holds a valid state after a step: no cache for the next mask
+        nxt = (dita.dita_plan_mask(plan, s + 1) if compose_ahead == "step" and s + 1 < steps
+               else None)
+        o, lse, info = dita.dita_attn_step(cache, q_dev, ks, vs, mask, s, compose_next=nxt)
         kp, vp = split_parts(k, wl), split_parts(v, wl)
         o_ref, lse_ref, nf = ref_cache.step(q_ref, kp, vp, mask, s)
         assert info.n_fresh == nf == int((mask == 0).sum())
@@ -80,6 +85,9 @@ def run_schedule(wl, dev, steps=None, seed=0, compose_ahead=False):
         eo, el = assert_state_close(host(o), host(lse), o_ref, lse_ref, wl.dtype,
                                     f"{wl.name} step {s} output")
         for p in np.flatnonzero(mask == 0):
+            first, last = cache.group(int(p))
+            if last > first:  # composed by the step already: compared below as a group
+                continue
             so, sl = cache.slot(int(p))
             ro, rl = ref_cache.slot(int(p))
             assert_state_close(host(so), host(sl), ro, rl, wl.dtype,
@@ -88,9 +96,13 @@ def run_schedule(wl, dev, steps=None, seed=0, compose_ahead=False):
         worst = [max(worst[0], eo), max(worst[1], el)]
         say(f"[{wl.name}] step {s}: fresh {nf}/{wl.P}  O err {eo:.2e}  LSE err {el:.2e}")
         if compose_ahead and s + 1 < steps:
-            nxt = dita.dita_plan_mask(plan, s + 1, cache)
-            assert np.array_equal(nxt, oracle_mask(ref_plan, s + 1, ref_cache.valid))
-            assert cache.compose_runs(nxt) == ref_cache.compose_runs(nxt)
+            if nxt is None:
+                nxt = dita.dita_plan_mask(plan, s + 1, cache)
+                assert np.array_equal(nxt, oracle_mask(ref_plan, s + 1, ref_cache.valid))
+                assert cache.compose_runs(nxt) == ref_cache.compose_runs(nxt)
+            else:
+                assert np.array_equal(nxt, oracle_mask(ref_plan, s + 1, ref_cache.valid))
+                assert info.composed == ref_cache.compose_runs(nxt)
             for p in ref_cache.leaders():
                 first, last = ref_cache.group_range(p)
                 assert cache.group(p) == (first, last)
@@ -111,7 +123,7 @@ def test_single_step_workload(dev, name):
         assert fresh == expect_fresh[name]
 
 
-@pytest.mark.parametrize("compose_ahead", [False, True])
+@pytest.mark.parametrize("compose_ahead", [False, True, "step"])
 def test_dit75k_anchor_schedule(dev, compose_ahead):
     wl = workloads.get("dit75k_bf16")
     worst, fresh, _ = run_schedule(wl, dev, compose_ahead=compose_ahead)
