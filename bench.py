@@ -9,7 +9,10 @@ bf16, P=16 context partitions of 4725 tokens; the rank owns partition 0 and
 recomputes partitions within distance 2, with a full refresh (anchor) every
 5th step.  The K/V of all 10 steps of that schedule are generated up front
 and resident in HBM before the timed region; timed step i uses the inputs
-and mask of schedule step (warmup + i) mod 10.
+and mask of schedule step (warmup + i) mod 10.  Before the warm-up steps,
+whole schedule cycles run untimed for --device-warmup seconds (the GPU comes
+out of the host-side input generation idle and its clock takes a few hundred
+ms of this load to settle); the JSON line reports them as device_warmup.
 
 Prints ONE JSON line:  value = fresh-block attention TFLOP/s over the whole
 timed job (fresh-block flops / wall time of the K steps), ms_per_step, the
@@ -17,11 +20,11 @@ roofline of the dominant kernel (the fresh-attention launch, timed with HIP
 events on its own stream), the merge's bandwidth, and the fp64 CPU oracle
 timed on a bounded sample of the same step.
 
-By default (--compose-ahead 1) each step is followed, inside the timed
-region, by the composition of the partitions the next step will reuse into
-groups (Dynamic Group Compose), so a step's merge reads one state per group;
---premerge 1 instead (or also) merges the reused states on a second stream
-while the fresh attention runs.
+By default (--compose-ahead 1) each step also composes the partitions the
+next step will reuse into groups (Dynamic Group Compose; the step's
+compose_next option, the largest run in the same pass as its final merge),
+so a step's merge reads one state per group; --premerge 1 instead (or also)
+merges the reused states on a second stream while the fresh attention runs.
 
 With --trajectory the schedule also runs once from a cold cache beside an
 all-fresh reference computed by the same library on the same K/V (every
